@@ -1,0 +1,27 @@
+"""HiSparse swap-in resolver for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libhisparse.so`` (C ABI in ``include/hisparse.h``).
+Every step of the resolver and of the sparse-MLA decode runs in the HIP
+kernels of that library; this package only marshals arguments (torch tensors
+for device memory, torch streams) and checks shapes and dtypes so that a
+wrong tensor is rejected on the host instead of being read out of bounds on
+the GPU.  There is no fallback: if the library is missing, importing the
+binding raises.
+"""
+from ._binding import (  # noqa: F401
+    HisparseError,
+    HostBuffer,
+    PoolConfig,
+    STAT_NAMES,
+    hisparse_destroy_pool,
+    hisparse_gather_copy,
+    hisparse_host_alloc,
+    hisparse_host_free,
+    hisparse_init_pool,
+    hisparse_last_error,
+    hisparse_resolve,
+    hisparse_resolve_plan,
+    hisparse_sparse_mla_decode,
+    library_path,
+    load_library,
+)

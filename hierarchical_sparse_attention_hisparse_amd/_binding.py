@@ -1,0 +1,275 @@
+"""ctypes binding of libhisparse.so: argument marshalling and host-side shape
+checks only.  Names match the C entry points of include/hisparse.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libhisparse.so")
+_lib = None
+
+STAT_NAMES = ("hot_hits", "misses", "resident_hits", "fast_path", "tripwires")
+
+
+class HisparseError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__("%s failed (code %d): %s" % (where, code, msg))
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [
+        ("max_requests", ctypes.c_int32), ("slots", ctypes.c_int32),
+        ("max_top_k", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+        ("row_bytes", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("resident_pages", ctypes.c_int64), ("max_seq_len", ctypes.c_int64),
+    ]
+
+
+@dataclass
+class PoolConfig:
+    max_requests: int
+    slots: int
+    max_top_k: int
+    max_batch: int
+    row_bytes: int = 656
+    num_layers: int = 1
+    page_size: int = 0
+    resident_pages: int = 0
+    max_seq_len: int = 0
+
+    def _c(self) -> _Config:
+        return _Config(self.max_requests, self.slots, self.max_top_k, self.max_batch,
+                       self.row_bytes, self.num_layers, self.page_size, 0,
+                       self.resident_pages, self.max_seq_len)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the built library; raises if it is missing (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libhisparse.so is not built: run `python -m "
+                          "hierarchical_sparse_attention_hisparse_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    V, I, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64
+    lib.hisparse_last_error.restype = ctypes.c_char_p
+    lib.hisparse_last_error.argtypes = []
+    lib.hisparse_host_alloc.restype = I
+    lib.hisparse_host_alloc.argtypes = [ctypes.c_size_t, ctypes.POINTER(V)]
+    lib.hisparse_host_free.restype = I
+    lib.hisparse_host_free.argtypes = [V]
+    lib.hisparse_init_pool.restype = I
+    lib.hisparse_init_pool.argtypes = [ctypes.POINTER(_Config), V, V, V, I64, ctypes.POINTER(V)]
+    lib.hisparse_destroy_pool.restype = None
+    lib.hisparse_destroy_pool.argtypes = [V]
+    resolve_args = [V, V, I32, I32, V, V, V, V, V, V, V, V, V, V]
+    lib.hisparse_resolve.restype = I
+    lib.hisparse_resolve.argtypes = resolve_args
+    lib.hisparse_resolve_plan.restype = I
+    lib.hisparse_resolve_plan.argtypes = resolve_args
+    lib.hisparse_gather_copy.restype = I
+    lib.hisparse_gather_copy.argtypes = [V, V, I32, I32, I32, V]
+    lib.hisparse_sparse_mla_decode.restype = I
+    lib.hisparse_sparse_mla_decode.argtypes = [V, V, I32, I32, I32, I32, V, V,
+                                               ctypes.c_float, V]
+    _lib = lib
+    return lib
+
+
+def hisparse_last_error() -> str:
+    return load_library().hisparse_last_error().decode("utf-8", "replace")
+
+
+def _check_rc(rc: int, where: str):
+    if rc != 0:
+        raise HisparseError(rc, where, hisparse_last_error())
+
+
+# ------------------------------------------------------------ host memory --
+
+def hisparse_host_alloc(nbytes: int) -> int:
+    p = ctypes.c_void_p()
+    _check_rc(load_library().hisparse_host_alloc(nbytes, ctypes.byref(p)), "hisparse_host_alloc")
+    return int(p.value)
+
+
+def hisparse_host_free(ptr: int):
+    _check_rc(load_library().hisparse_host_free(ctypes.c_void_p(ptr)), "hisparse_host_free")
+
+
+class HostBuffer:
+    """Pinned, device-mapped host memory from hisparse_host_alloc, viewable as
+    a numpy array or a CPU torch tensor (views must not outlive it)."""
+
+    def __init__(self, nbytes: int):
+        self.nbytes = int(nbytes)
+        self.ptr = hisparse_host_alloc(self.nbytes)
+
+    def numpy(self, shape=None, dtype=np.uint8) -> np.ndarray:
+        buf = (ctypes.c_uint8 * self.nbytes).from_address(self.ptr)
+        a = np.frombuffer(buf, dtype=np.uint8)
+        a = a.view(dtype)
+        return a.reshape(shape) if shape is not None else a
+
+    def torch(self, shape=None, dtype=np.uint8):
+        import torch
+        return torch.from_numpy(self.numpy(shape, dtype))
+
+    def free(self):
+        if self.ptr:
+            hisparse_host_free(self.ptr)
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------- marshalling --
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False):
+    import torch
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device (cuda) tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t.data_ptr()
+
+
+class _Pool:
+    def __init__(self, handle: int, cfg: PoolConfig, device_pool_rows: int):
+        self.handle = handle
+        self.cfg = cfg
+        self.device_pool_rows = device_pool_rows
+
+
+def hisparse_init_pool(config: PoolConfig, host_pools, host_pool_rows, device_pools,
+                       device_pool_rows: int) -> _Pool:
+    """host_pools: HostBuffer objects or pinned host addresses (one per layer);
+    device_pools: uint8 cuda tensors [device_pool_rows, row_bytes]."""
+    import torch
+    L = config.num_layers
+    if len(host_pools) != L or len(host_pool_rows) != L or len(device_pools) != L:
+        raise ValueError("need one host pool, row count and device pool per layer")
+    hp = (ctypes.c_void_p * L)()
+    for l, h in enumerate(host_pools):
+        addr = h.ptr if isinstance(h, HostBuffer) else int(h)
+        if isinstance(h, HostBuffer) and h.nbytes < host_pool_rows[l] * config.row_bytes:
+            raise ValueError("host pool %d holds fewer than host_pool_rows rows" % l)
+        hp[l] = addr
+    rows = (ctypes.c_int64 * L)(*[int(x) for x in host_pool_rows])
+    dp = (ctypes.c_void_p * L)()
+    for l, d in enumerate(device_pools):
+        dp[l] = _dev(d, torch.uint8, (device_pool_rows, config.row_bytes), "device_pools[%d]" % l)
+    c = config._c()
+    out = ctypes.c_void_p()
+    _check_rc(load_library().hisparse_init_pool(ctypes.byref(c), ctypes.cast(hp, ctypes.c_void_p),
+                                                 ctypes.cast(rows, ctypes.c_void_p),
+                                                 ctypes.cast(dp, ctypes.c_void_p),
+                                                 device_pool_rows, ctypes.byref(out)),
+              "hisparse_init_pool")
+    return _Pool(int(out.value), config, device_pool_rows)
+
+
+def hisparse_destroy_pool(pool: _Pool):
+    if pool is not None and pool.handle:
+        load_library().hisparse_destroy_pool(ctypes.c_void_p(pool.handle))
+        pool.handle = 0
+
+
+def _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                  resident_block_table, slot_tokens, lru_slots, lru_clock,
+                  device_buffer_locs, stats):
+    import torch
+    c = pool.cfg
+    R, S = c.max_requests, c.slots
+    max_pages = (c.max_seq_len + c.page_size - 1) // c.page_size if c.page_size > 0 else 0
+    return [
+        _dev(req_idx, torch.int32, (batch,), "req_idx"),
+        _dev(top_k_tokens, torch.int32, (batch, top_k), "top_k_tokens"),
+        _dev(seq_lens, torch.int32, (batch,), "seq_lens"),
+        _dev(host_cache_locs, torch.int64, (R, c.max_seq_len), "host_cache_locs"),
+        _dev(resident_block_table, torch.int32, (R, max_pages), "resident_block_table",
+             allow_none=True),
+        _dev(slot_tokens, torch.int32, (R, S), "slot_tokens"),
+        _dev(lru_slots, torch.int32, (R, S), "lru_slots"),
+        _dev(lru_clock, torch.int32, (R,), "lru_clock"),
+        _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs"),
+        _dev(stats, torch.int64, (5,), "stats", allow_none=True),
+    ]
+
+
+def hisparse_resolve(pool, stream, batch, top_k, req_idx, top_k_tokens, seq_lens,
+                     host_cache_locs, resident_block_table, slot_tokens, lru_slots,
+                     lru_clock, device_buffer_locs, stats=None):
+    """One decode step (plan + miss copy); stats is an int64 cuda tensor [5]
+    holding the uint64 counters, or None."""
+    ptrs = _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                         resident_block_table, slot_tokens, lru_slots, lru_clock,
+                         device_buffer_locs, stats)
+    _check_rc(load_library().hisparse_resolve(pool.handle, _stream_handle(stream), batch, top_k,
+                                              *ptrs), "hisparse_resolve")
+
+
+def hisparse_resolve_plan(pool, stream, batch, top_k, req_idx, top_k_tokens, seq_lens,
+                          host_cache_locs, resident_block_table, slot_tokens, lru_slots,
+                          lru_clock, device_buffer_locs, stats=None):
+    ptrs = _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                         resident_block_table, slot_tokens, lru_slots, lru_clock,
+                         device_buffer_locs, stats)
+    _check_rc(load_library().hisparse_resolve_plan(pool.handle, _stream_handle(stream), batch,
+                                                   top_k, *ptrs), "hisparse_resolve_plan")
+
+
+def hisparse_gather_copy(pool, stream, batch, layer_begin=0, layer_end=None, stats=None):
+    import torch
+    if layer_end is None:
+        layer_end = pool.cfg.num_layers
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    _check_rc(load_library().hisparse_gather_copy(pool.handle, _stream_handle(stream), batch,
+                                                  layer_begin, layer_end, sp),
+              "hisparse_gather_copy")
+
+
+def hisparse_sparse_mla_decode(pool, stream, batch, heads, top_k, layer, q_bf16,
+                               device_buffer_locs, softmax_scale, out_bf16):
+    import torch
+    qp = _dev(q_bf16, torch.bfloat16, (batch, heads, 576), "q_bf16")
+    lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs")
+    op = _dev(out_bf16, torch.bfloat16, (batch, heads, 512), "out_bf16")
+    _check_rc(load_library().hisparse_sparse_mla_decode(pool.handle, _stream_handle(stream),
+                                                        batch, heads, top_k, layer, qp, lp,
+                                                        ctypes.c_float(softmax_scale), op),
+              "hisparse_sparse_mla_decode")

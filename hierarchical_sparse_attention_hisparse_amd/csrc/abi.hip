@@ -1,0 +1,365 @@
+// abi.hip -- the extern "C" entry points of libhisparse (see include/hisparse.h):
+// host-side validation, the pool object and its device workspace, and the
+// kernel launches.  No entry point that takes a stream synchronises or reads
+// device memory back.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/hisparse.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace hisparse;
+
+struct hisparse_pool {
+  hisparse_pool_config cfg;
+  int device;
+  int64_t device_pool_rows;
+  int64_t max_pages;
+  // device workspace
+  int64_t* plan_src;   // [max_batch][max_top_k]
+  int32_t* plan_dst;   // [max_batch][max_top_k]
+  int32_t* plan_cnt;   // [max_batch]
+  unsigned char** d_host_ptrs;  // [L] device-mapped host pool pointers
+  unsigned char** d_dev_ptrs;   // [L]
+  int64_t* d_host_rows;         // [L]
+  // host copies
+  unsigned char** dev_ptrs;     // [L]
+  float* dec_part_o;            // decode split partials (allocated lazily per shape)
+  float* dec_part_ml;
+  size_t dec_part_bytes;
+  int copy_chunks;
+};
+
+namespace {
+
+thread_local char g_err[1024];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return HISPARSE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HISPARSE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_device(const hisparse_pool* pool) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != pool->device)
+    return fail(HISPARSE_EINVAL, "current device %d is not the pool's device %d", dev,
+                pool->device);
+  return HISPARSE_OK;
+}
+
+int check_resolve_args(const hisparse_pool* pool, int32_t batch, int32_t top_k,
+                       const int32_t* req_idx, const int32_t* top_k_tokens,
+                       const int32_t* seq_lens, const int64_t* host_cache_locs,
+                       const int32_t* bt, int32_t* slot_tokens, int32_t* lru_slots,
+                       int32_t* lru_clock, int32_t* out, uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  if (batch < 0 || batch > pool->cfg.max_batch)
+    return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
+  if (top_k < 0 || top_k > pool->cfg.max_top_k)
+    return fail(HISPARSE_EINVAL, "top_k %d outside [0, max_top_k=%d]", top_k, pool->cfg.max_top_k);
+  if (batch == 0) return HISPARSE_OK;
+  const void* req[] = {req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                       slot_tokens, lru_slots, lru_clock, out};
+  const char* names[] = {"req_idx", "top_k_tokens", "seq_lens", "host_cache_locs",
+                         "slot_tokens", "lru_slots", "lru_clock", "device_buffer_locs"};
+  for (int i = 0; i < 8; ++i) {
+    const bool topk_array = (i == 1 || i == 7);
+    if (req[i] == nullptr && topk_array && top_k == 0) continue;  // empty rows
+    if (req[i] == nullptr) return fail(HISPARSE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned(req[i], i == 3 ? 8 : 4))
+      return fail(HISPARSE_EINVAL, "%s is not aligned to its element size", names[i]);
+  }
+  if (bt != nullptr) {
+    if (pool->cfg.page_size <= 0)
+      return fail(HISPARSE_EINVAL, "resident_block_table given but the pool has page_size 0");
+    if (!aligned(bt, 4)) return fail(HISPARSE_EINVAL, "resident_block_table is not 4-byte aligned");
+  }
+  if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
+  return HISPARSE_OK;
+}
+
+int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t top_k,
+                const int32_t* req_idx, const int32_t* top_k_tokens, const int32_t* seq_lens,
+                const int64_t* host_cache_locs, const int32_t* bt, int32_t* slot_tokens,
+                int32_t* lru_slots, int32_t* lru_clock, int32_t* out, uint64_t* stats) {
+  ResolveParams p;
+  p.R = pool->cfg.max_requests;
+  p.S = pool->cfg.slots;
+  p.k = top_k;
+  p.P = pool->cfg.page_size;
+  p.max_seq_len = pool->cfg.max_seq_len;
+  p.max_pages = pool->max_pages;
+  p.resident_pages = pool->cfg.resident_pages;
+  p.req_idx = req_idx;
+  p.topk = top_k_tokens;
+  p.seq_lens = seq_lens;
+  p.locs = host_cache_locs;
+  p.bt = bt;
+  p.st = slot_tokens;
+  p.lru = lru_slots;
+  p.clk = lru_clock;
+  p.out = out;
+  p.stats = (unsigned long long*)stats;
+  p.plan_src = pool->plan_src;
+  p.plan_dst = pool->plan_dst;
+  p.plan_cnt = pool->plan_cnt;
+  p.plan_stride = pool->cfg.max_top_k;
+  hipError_t e = launch_resolve(p, batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "resolve kernel launch");
+  return HISPARSE_OK;
+}
+
+int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t lb, int32_t le,
+                uint64_t* stats) {
+  CopyParams c;
+  c.host_pools = pool->d_host_ptrs;
+  c.dev_pools = pool->d_dev_ptrs;
+  c.host_rows = pool->d_host_rows;
+  c.plan_src = pool->plan_src;
+  c.plan_dst = pool->plan_dst;
+  c.plan_cnt = pool->plan_cnt;
+  c.stats = (unsigned long long*)stats;
+  c.plan_stride = pool->cfg.max_top_k;
+  c.units = pool->cfg.row_bytes / 16;
+  c.chunks = pool->copy_chunks;
+  c.layer_begin = lb;
+  hipError_t e = launch_gather_copy(c, batch, le - lb, stream);
+  if (e != hipSuccess) return hip_fail(e, "gather copy kernel launch");
+  return HISPARSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hisparse_last_error(void) { return g_err; }
+
+int hisparse_host_alloc(size_t bytes, void** out) {
+  if (!out) return fail(HISPARSE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (bytes == 0) return fail(HISPARSE_EINVAL, "bytes is 0");
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess || p == nullptr)
+    return fail(HISPARSE_ENOMEM, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  *out = p;
+  return ok();
+}
+
+int hisparse_host_free(void* ptr) {
+  if (!ptr) return ok();
+  hipError_t e = hipHostFree(ptr);
+  if (e != hipSuccess) return hip_fail(e, "hipHostFree");
+  return ok();
+}
+
+int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
+                       const int64_t* host_pool_rows, void* const* device_pools,
+                       int64_t device_pool_rows, hisparse_pool** out) {
+  if (!out) return fail(HISPARSE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(HISPARSE_EINVAL, "config is NULL");
+  const hisparse_pool_config c = *cfg;
+  if (c.max_requests <= 0) return fail(HISPARSE_EINVAL, "max_requests must be > 0");
+  if (c.slots <= 0 || c.slots > kMaxSlots)
+    return fail(HISPARSE_EINVAL, "slots %d outside [1, %d]", c.slots, kMaxSlots);
+  if (c.max_top_k <= 0 || c.max_top_k > c.slots || c.max_top_k > kMaxTopK)
+    return fail(HISPARSE_EINVAL, "max_top_k %d outside [1, min(slots, %d)]", c.max_top_k, kMaxTopK);
+  if (c.max_batch <= 0) return fail(HISPARSE_EINVAL, "max_batch must be > 0");
+  if (c.row_bytes <= 0 || c.row_bytes % 16 != 0)
+    return fail(HISPARSE_EINVAL, "row_bytes %d is not a positive multiple of 16", c.row_bytes);
+  if (c.num_layers <= 0) return fail(HISPARSE_EINVAL, "num_layers must be > 0");
+  if (c.page_size < 0 || c.resident_pages < 0 || c.reserved != 0)
+    return fail(HISPARSE_EINVAL, "page_size / resident_pages must be >= 0, reserved must be 0");
+  if (c.resident_pages > 0 && c.page_size == 0)
+    return fail(HISPARSE_EINVAL, "resident_pages > 0 needs page_size > 0");
+  if (c.max_seq_len <= 0 || c.max_seq_len > INT32_MAX)
+    return fail(HISPARSE_EINVAL, "max_seq_len must be in [1, 2^31)");
+  const int64_t need_rows = (int64_t)c.max_requests * c.slots + c.resident_pages * (int64_t)c.page_size;
+  if (device_pool_rows < need_rows || device_pool_rows > INT32_MAX)
+    return fail(HISPARSE_EINVAL, "device_pool_rows %lld must be >= R*S + resident_pages*P = %lld and < 2^31",
+                (long long)device_pool_rows, (long long)need_rows);
+  const ResolveLds lay = resolve_lds_layout(c.slots, c.max_top_k);
+  if (lay.total > kLdsBudget)
+    return fail(HISPARSE_EUNSUPPORTED, "slots %d with max_top_k %d need %zu bytes of LDS (> %zu)",
+                c.slots, c.max_top_k, lay.total, kLdsBudget);
+  if (!host_pools || !host_pool_rows || !device_pools)
+    return fail(HISPARSE_EINVAL, "pool arrays are NULL");
+  const int L = c.num_layers;
+  for (int l = 0; l < L; ++l) {
+    if (host_pool_rows[l] < 0) return fail(HISPARSE_EINVAL, "host_pool_rows[%d] < 0", l);
+    if (host_pool_rows[l] > 0 && (!host_pools[l] || !aligned(host_pools[l], 16)))
+      return fail(HISPARSE_EINVAL, "host_pools[%d] is NULL or not 16-byte aligned", l);
+    if (!device_pools[l] || !aligned(device_pools[l], 16))
+      return fail(HISPARSE_EINVAL, "device_pools[%d] is NULL or not 16-byte aligned", l);
+  }
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+  // Device-side views of the pinned host pools.
+  unsigned char** hdev = (unsigned char**)calloc(L, sizeof(void*));
+  unsigned char** ddev = (unsigned char**)calloc(L, sizeof(void*));
+  if (!hdev || !ddev) {
+    free(hdev);
+    free(ddev);
+    return fail(HISPARSE_ENOMEM, "host allocation failed");
+  }
+  for (int l = 0; l < L; ++l) {
+    ddev[l] = (unsigned char*)device_pools[l];
+    if (host_pool_rows[l] == 0) continue;
+    void* dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, host_pools[l], 0);
+    if (e != hipSuccess || dp == nullptr) {
+      free(hdev);
+      free(ddev);
+      (void)hipGetLastError();
+      return fail(HISPARSE_EINVAL,
+                  "host_pools[%d] is not pinned, device-mapped host memory (use hisparse_host_alloc): %s",
+                  l, hipGetErrorString(e));
+    }
+    hdev[l] = (unsigned char*)dp;
+  }
+
+  hisparse_pool* pool = (hisparse_pool*)calloc(1, sizeof(hisparse_pool));
+  if (!pool) {
+    free(hdev);
+    free(ddev);
+    return fail(HISPARSE_ENOMEM, "host allocation failed");
+  }
+  pool->cfg = c;
+  pool->device = dev;
+  pool->device_pool_rows = device_pool_rows;
+  pool->max_pages = c.page_size > 0 ? (c.max_seq_len + c.page_size - 1) / c.page_size : 0;
+  pool->dev_ptrs = ddev;
+  pool->copy_chunks = 16;
+
+  const size_t entries = (size_t)c.max_batch * c.max_top_k;
+  const size_t bytes_src = entries * 8, bytes_dst = entries * 4, bytes_cnt = (size_t)c.max_batch * 4;
+  const size_t bytes_tab = (size_t)L * 8;
+  unsigned char* ws = nullptr;
+  const size_t total = align16(bytes_src) + align16(bytes_dst) + align16(bytes_cnt) + 3 * align16(bytes_tab);
+  e = hipMalloc((void**)&ws, total);
+  if (e != hipSuccess) {
+    free(hdev);
+    free(ddev);
+    free(pool);
+    (void)hipGetLastError();
+    return fail(HISPARSE_ENOMEM, "hipMalloc(%zu) for the plan workspace: %s", total, hipGetErrorString(e));
+  }
+  size_t o = 0;
+  pool->plan_src = (int64_t*)(ws + o);        o += align16(bytes_src);
+  pool->plan_dst = (int32_t*)(ws + o);        o += align16(bytes_dst);
+  pool->plan_cnt = (int32_t*)(ws + o);        o += align16(bytes_cnt);
+  pool->d_host_ptrs = (unsigned char**)(ws + o); o += align16(bytes_tab);
+  pool->d_dev_ptrs = (unsigned char**)(ws + o);  o += align16(bytes_tab);
+  pool->d_host_rows = (int64_t*)(ws + o);
+  e = hipMemset(ws, 0, total);
+  if (e == hipSuccess) e = hipMemcpy(pool->d_host_ptrs, hdev, bytes_tab, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(pool->d_dev_ptrs, ddev, bytes_tab, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(pool->d_host_rows, host_pool_rows, bytes_tab, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = prepare_resolve(kLdsBudget);
+  free(hdev);
+  if (e != hipSuccess) {
+    (void)hipFree(ws);
+    free(ddev);
+    free(pool);
+    return hip_fail(e, "pool set-up");
+  }
+  *out = pool;
+  return ok();
+}
+
+void hisparse_destroy_pool(hisparse_pool* pool) {
+  if (!pool) return;
+  if (pool->plan_src) (void)hipFree(pool->plan_src);
+  if (pool->dec_part_o) (void)hipFree(pool->dec_part_o);
+  free(pool->dev_ptrs);
+  free(pool);
+}
+
+int hisparse_resolve_plan(hisparse_pool* pool, void* stream, int32_t batch, int32_t top_k,
+                          const int32_t* req_idx, const int32_t* top_k_tokens,
+                          const int32_t* seq_lens, const int64_t* host_cache_locs,
+                          const int32_t* resident_block_table, int32_t* slot_tokens,
+                          int32_t* lru_slots, int32_t* lru_clock, int32_t* device_buffer_locs,
+                          uint64_t* stats) {
+  int rc = check_resolve_args(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                              resident_block_table, slot_tokens, lru_slots, lru_clock,
+                              device_buffer_locs, stats);
+  if (rc != HISPARSE_OK) return rc;
+  if (batch == 0) return ok();
+  if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
+  rc = launch_plan(pool, (hipStream_t)stream, batch, top_k, req_idx, top_k_tokens, seq_lens,
+                   host_cache_locs, resident_block_table, slot_tokens, lru_slots, lru_clock,
+                   device_buffer_locs, stats);
+  return rc == HISPARSE_OK ? ok() : rc;
+}
+
+int hisparse_gather_copy(hisparse_pool* pool, void* stream, int32_t batch, int32_t layer_begin,
+                         int32_t layer_end, uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  if (batch < 0 || batch > pool->cfg.max_batch)
+    return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
+  if (layer_begin < 0 || layer_end > pool->cfg.num_layers || layer_begin > layer_end)
+    return fail(HISPARSE_EINVAL, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
+                pool->cfg.num_layers);
+  if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
+  if (batch == 0 || layer_begin == layer_end) return ok();
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  rc = launch_copy(pool, (hipStream_t)stream, batch, layer_begin, layer_end, stats);
+  return rc == HISPARSE_OK ? ok() : rc;
+}
+
+int hisparse_resolve(hisparse_pool* pool, void* stream, int32_t batch, int32_t top_k,
+                     const int32_t* req_idx, const int32_t* top_k_tokens, const int32_t* seq_lens,
+                     const int64_t* host_cache_locs, const int32_t* resident_block_table,
+                     int32_t* slot_tokens, int32_t* lru_slots, int32_t* lru_clock,
+                     int32_t* device_buffer_locs, uint64_t* stats) {
+  int rc = check_resolve_args(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                              resident_block_table, slot_tokens, lru_slots, lru_clock,
+                              device_buffer_locs, stats);
+  if (rc != HISPARSE_OK) return rc;
+  if (batch == 0) return ok();
+  if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
+  rc = launch_plan(pool, (hipStream_t)stream, batch, top_k, req_idx, top_k_tokens, seq_lens,
+                   host_cache_locs, resident_block_table, slot_tokens, lru_slots, lru_clock,
+                   device_buffer_locs, stats);
+  if (rc != HISPARSE_OK) return rc;
+  rc = launch_copy(pool, (hipStream_t)stream, batch, 0, pool->cfg.num_layers, stats);
+  return rc == HISPARSE_OK ? ok() : rc;
+}
+
+int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,
+                               int32_t top_k, int32_t layer, const void* q_bf16,
+                               const int32_t* device_buffer_locs, float softmax_scale,
+                               void* out_bf16) {
+  (void)stream; (void)q_bf16; (void)device_buffer_locs; (void)softmax_scale; (void)out_bf16;
+  (void)batch; (void)heads; (void)top_k; (void)layer;
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  return fail(HISPARSE_EUNSUPPORTED, "sparse-MLA decode is not built yet");
+}
+
+}  // extern "C"

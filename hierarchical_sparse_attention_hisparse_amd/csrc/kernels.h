@@ -1,0 +1,62 @@
+// kernels.h -- internal launch interfaces of libhisparse (not public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hisparse {
+
+struct ResolveParams {
+  int32_t R, S, k, P;
+  int64_t max_seq_len, max_pages, resident_pages;
+  const int32_t* req_idx;
+  const int32_t* topk;
+  const int32_t* seq_lens;
+  const int64_t* locs;
+  const int32_t* bt;  // may be null
+  int32_t* st;
+  int32_t* lru;
+  int32_t* clk;
+  int32_t* out;
+  unsigned long long* stats;  // may be null
+  int64_t* plan_src;
+  int32_t* plan_dst;
+  int32_t* plan_cnt;
+  int32_t plan_stride;
+};
+
+struct CopyParams {
+  const unsigned char* const* host_pools;  // device array [L] of device-mapped host pointers
+  unsigned char* const* dev_pools;         // device array [L]
+  const int64_t* host_rows;                // device array [L]
+  const int64_t* plan_src;
+  const int32_t* plan_dst;
+  const int32_t* plan_cnt;
+  unsigned long long* stats;  // may be null
+  int32_t plan_stride;
+  int32_t units;       // row_bytes / 16
+  int32_t chunks;      // workgroups per batch row
+  int32_t layer_begin;
+};
+
+struct DecodeParams {
+  const unsigned char* pool;  // one layer's device pool
+  int64_t pool_rows;
+  int32_t row_bytes;
+  int32_t heads;
+  int32_t k;
+  float scale;
+  const uint16_t* q;     // bf16 bits [B][H][576]
+  const int32_t* locs;   // [B][k]
+  uint16_t* out;         // bf16 bits [B][H][512]
+  float* part_o;         // [B][H/16][splits][16][512] partial outputs
+  float* part_ml;        // [B][H/16][splits][16][2] partial max / sum
+  int32_t splits;
+};
+
+hipError_t prepare_resolve(size_t lds_bytes);
+hipError_t launch_resolve(const ResolveParams& p, int batch, hipStream_t stream);
+hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream);
+hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
+
+}  // namespace hisparse

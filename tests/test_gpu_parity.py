@@ -1,0 +1,152 @@
+"""GPU parity of the HIP resolver against the CPU oracle (bit-exact).
+
+Every step compares device_buffer_locs, slot_tokens, lru_slots, lru_clock,
+the five counters and the device rows named by that step's output; the
+whole device pools are compared at the end.  Calls go through the C ABI
+(ctypes binding of libhisparse.so).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hisparse_amd as hs
+from tests.harness import Pair, make_host_pools, run_parity
+from workloads import synth, config1_tiny
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(name):
+    def f(step):
+        if step % 8 == 0:
+            print("[%s] step %d ok" % (name, step), flush=True)
+    return f
+
+
+def test_config1_tiny_all_steps():
+    print("[config1] 4 req, n=8192, k=256, S=512, 32 steps", flush=True)
+    w = config1_tiny()
+    stats = run_parity(w, log=_log("config1"))
+    assert stats[1] > 0 and stats[0] > 0
+
+
+def test_ragged_shapes_fast_path_transition_and_padding():
+    """S and k not multiples of the wavefront or block size, padding rows,
+    fast-path rows that cross seq_len == S during the run, rows with
+    seq_len <= k (padded top-k)."""
+    print("[ragged] S=200 k=77 steps=8", flush=True)
+    w = synth("ragged", 21, R=7, S=200, k=77, steps=8,
+              n0=[1000, 300, 198, 200, 5000, 60], grow=1, keep=50, recent=10,
+              recent_window=100, padding_rows=2)
+    run_parity(w, log=_log("ragged"))
+
+
+def test_multi_layer_shared_plan():
+    print("[layers] L=3", flush=True)
+    w = synth("layers", 22, R=4, S=256, k=128, steps=6, n0=[4000, 3000, 2500, 9000], L=3,
+              keep=100, recent=8, recent_window=64)
+    run_parity(w, log=_log("layers"))
+
+
+def test_resident_pages_small():
+    print("[resident] P=16 tail=64", flush=True)
+    w = synth("resident", 23, R=6, S=256, k=128, steps=6, n0=[2048] * 6, keep=90,
+              P=16, resident_tail=256)
+    stats = run_parity(w, log=_log("resident"))
+    assert stats[2] > 0
+
+
+def test_top_k_equals_slots():
+    print("[k=S] S=k=2048", flush=True)
+    w = synth("kS", 24, R=3, S=2048, k=2048, steps=4, n0=[50000, 40000, 30000], keep=1800)
+    run_parity(w, log=_log("k=S"))
+
+
+def test_zero_top_k_and_empty_batch():
+    w = synth("k0", 25, R=2, S=64, k=8, steps=1, n0=[500, 100])
+    bufs = make_host_pools(w)
+    pair = Pair(w, bufs)
+    try:
+        empty = torch.empty((w.B, 0), dtype=torch.int32, device="cuda")
+        hs.hisparse_resolve(pair.pool, None, w.B, 0, pair.req_idx, empty, pair.seq[0], pair.locs,
+                            None, pair.st, pair.lru, pair.clk, empty, pair.stats)
+        e1 = torch.empty((0,), dtype=torch.int32, device="cuda")
+        hs.hisparse_resolve(pair.pool, None, 0, w.k, e1, torch.empty((0, w.k), dtype=torch.int32,
+                            device="cuda"), e1, pair.locs, None, pair.st, pair.lru, pair.clk,
+                            torch.empty((0, w.k), dtype=torch.int32, device="cuda"), pair.stats)
+        torch.cuda.synchronize()
+        assert pair.clk.cpu().tolist() == [1, 1]          # one active call each
+        assert pair.stats.cpu().tolist() == [0, 0, 0, 0, 0]
+    finally:
+        pair.close()
+
+
+def test_corrupt_state_and_tripwires():
+    """Corrupt slot map (markers below -1, one position in two slots, tokens
+    past seq_len), scrambled stamps (forces the full-sort victim path),
+    out-of-range host rows and block-table ids, a request index past R."""
+    print("[corrupt]", flush=True)
+    w = synth("corrupt", 26, R=5, S=96, k=40, steps=5, n0=[3000, 2000, 1500, 800],
+              keep=30, P=8, resident_tail=64, padding_rows=1)
+    rng = np.random.default_rng(5)
+    w.req_idx[w.req_idx < 0] = w.R + 2
+    bufs = make_host_pools(w)
+    pair = Pair(w, bufs)      # admission uses the clean tables
+    try:
+        locs = w.host_cache_locs
+        locs[rng.random(locs.shape) < 0.05] = -7
+        locs[rng.random(locs.shape) < 0.05] = w.host_pool_rows + 3
+        bt = w.block_table
+        bt[(bt >= 0) & (rng.random(bt.shape) < 0.2)] = w.resident_pages + 1
+        pair.locs.copy_(torch.from_numpy(locs))
+        pair.bt.copy_(torch.from_numpy(bt))
+        st = rng.integers(-4, 3500, size=(w.R, w.S)).astype(np.int32)
+        st[0, 3] = st[0, 70] = 1234
+        lru = rng.permutation(w.R * w.S).reshape(w.R, w.S).astype(np.int32) - 200
+        pair.st.copy_(torch.from_numpy(st))
+        pair.lru.copy_(torch.from_numpy(lru))
+        pair.ost.slot_tokens[:] = st
+        pair.ost.lru_slots[:] = lru
+        for step in range(w.steps):
+            dst, src = pair.gpu_step(step)
+            o = pair.oracle_step(step, dst, src)
+            torch.cuda.synchronize()
+            pair.compare_step(step, o)
+        pair.compare_pools()
+        assert pair.ost.stats[4] > 0
+    finally:
+        pair.close()
+
+
+def test_host_side_errors():
+    w = synth("err", 27, R=2, S=64, k=8, steps=1, n0=[500, 100])
+    bufs = make_host_pools(w)
+    pair = Pair(w, bufs, with_oracle=False)
+    try:
+        big = torch.zeros((w.B + 5, w.k), dtype=torch.int32, device="cuda")
+        with pytest.raises(ValueError):     # shape check in the binding
+            hs.hisparse_resolve(pair.pool, None, w.B, w.k, pair.req_idx, big, pair.seq[0],
+                                pair.locs, None, pair.st, pair.lru, pair.clk, pair.out, None)
+        lib = hs.load_library()
+        import ctypes
+        rc = lib.hisparse_resolve(ctypes.c_void_p(pair.pool.handle), None, w.B + 100, w.k,
+                                  *([None] * 10))
+        assert rc == -1 and "max_batch" in hs.hisparse_last_error()
+        rc = lib.hisparse_gather_copy(ctypes.c_void_p(pair.pool.handle), None, w.B, 0, 5, None)
+        assert rc == -1
+        # a host pool that is not pinned memory is refused at init
+        plain = np.zeros((w.host_pool_rows, 656), np.uint8)
+        cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                            max_seq_len=w.max_seq_len)
+        with pytest.raises(hs.HisparseError):
+            hs.hisparse_init_pool(cfg, [plain.ctypes.data], [w.host_pool_rows],
+                                  pair.dev_pools, w.dev_pool_rows)
+        bad = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.S + 1, max_batch=w.B,
+                            max_seq_len=w.max_seq_len)
+        with pytest.raises(hs.HisparseError):
+            hs.hisparse_init_pool(bad, bufs, [w.host_pool_rows], pair.dev_pools, w.dev_pool_rows)
+        # the pool still works after the refused calls
+        pair.gpu_step(0)
+        torch.cuda.synchronize()
+    finally:
+        pair.close()

@@ -219,6 +219,8 @@ def synth(name, seed, *, R, S, k, steps, n0, L=1, grow=0, keep=0, recent=0,
         for r in range(R):
             n_r = int(n_final_req[r])
             first = n_r // P - tail_pages
+            if n_r == 0 or first < 0:
+                continue                # inactive or too short: no resident tail
             block_table[r, first:first + tail_pages] = phys[r * tail_pages:(r + 1) * tail_pages]
 
     return Workload(name=name, R=R, S=S, k=k, L=L, P=P, B=B, steps=steps,
@@ -290,7 +292,7 @@ def admission(w: Workload):
     dst, src = [], []
     for b in range(w.B):
         r = int(w.req_idx[b])
-        if r < 0:
+        if r < 0 or r >= w.R:
             continue
         n0 = int(w.seq_lens[0, b])
         if n0 <= w.S:
@@ -319,7 +321,7 @@ def decode_writes(w: Workload, step: int):
         return np.zeros(0, np.int64), np.zeros(0, np.int64)
     for b in range(w.B):
         r = int(w.req_idx[b])
-        if r < 0:
+        if r < 0 or r >= w.R:
             continue
         n_prev, n = int(w.seq_lens[step - 1, b]), int(w.seq_lens[step, b])
         if n <= w.S and n > n_prev:
