@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the HiSparse swap-in resolver on one MI355X.
+
+A step is one decode step of the resolver (hisparse_resolve = plan kernel +
+miss-copy kernel) over the DSA-decode workload: 64 long requests with
+seq_len U[32768, 131072] plus 8 short fast-path requests, top-k 2048,
+4096 hot slots, 656-byte fp8 sparse-MLA rows, 90 % of each step's top-k kept
+from the previous step, 5 % from the newest 2048 positions, 5 % uniform,
+seq_len + 1 per step.  Inputs (top-k traces, host_cache_locs, state) are in
+HBM and the host pool in pinned host memory before the timed region starts.
+
+Prints one JSON line: rows resolved per second over the timed steps, the
+roofline of the dominant kernel (the miss copy, bound by the host link),
+the roofline of the plan kernel (HBM), and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "top-k rows resolved/s at B=64,k=2048; miss-copy GB/s vs host-link roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+HOST_LINK_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction, published
+ROW_BYTES = 656
+KERNEL_SOURCES = {
+    "gather_copy": "hierarchical_sparse_attention_hisparse_amd/csrc/gather.hip",
+    "resolve": "hierarchical_sparse_attention_hisparse_amd/csrc/resolve.hip",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def src_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, used
+    only while the kernel source still matches the one that was profiled."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != src_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return t
+
+
+def measure_h2d_peak(torch, nbytes=1 << 30, reps=10):
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h.fill_(7)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 1e30
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        d.copy_(h, non_blocking=True)
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e))
+    del h, d
+    return nbytes / (best * 1e-3) / 1e9
+
+
+def setup_gpu(w, torch, hs, host_buf):
+    from workloads import admission, decode_writes
+    dev = torch.device("cuda")
+    pools = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)]
+    cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                        row_bytes=w.row_bytes, num_layers=w.L, page_size=w.P,
+                        resident_pages=w.resident_pages, max_seq_len=w.max_seq_len)
+    pool = hs.hisparse_init_pool(cfg, [host_buf], [w.host_pool_rows], pools, w.dev_pool_rows)
+    st, lru, clk, dst, src = admission(w)
+    # the forward pass's KV writes of fast-path requests for every step, ahead
+    extra = [decode_writes(w, s) for s in range(1, w.steps)]
+    dst = np.concatenate([dst] + [e[0] for e in extra])
+    src = np.concatenate([src] + [e[1] for e in extra])
+    host_t = host_buf.torch((w.host_pool_rows, w.row_bytes))
+    if len(dst):
+        pools[0].index_copy_(0, torch.from_numpy(dst).to(dev),
+                             host_t[torch.from_numpy(src)].to(dev))
+    g = dict(
+        pool=pool, pools=pools, st0=st, lru0=lru, clk0=clk, pre_dst=dst, pre_src=src,
+        st=torch.from_numpy(st).to(dev), lru=torch.from_numpy(lru).to(dev),
+        clk=torch.from_numpy(clk).to(dev), stats=torch.zeros(5, dtype=torch.int64, device=dev),
+        req=torch.from_numpy(w.req_idx).to(dev), locs=torch.from_numpy(w.host_cache_locs).to(dev),
+        topk=torch.from_numpy(w.top_k).to(dev), seq=torch.from_numpy(w.seq_lens).to(dev),
+        out=torch.empty((w.B, w.k), dtype=torch.int32, device=dev),
+    )
+    torch.cuda.synchronize()
+    return g
+
+
+def reset_state(g):
+    g["st"].copy_(g["st"].new_tensor(g["st0"]))
+    g["lru"].copy_(g["lru"].new_tensor(g["lru0"]))
+    g["clk"].copy_(g["clk"].new_tensor(g["clk0"]))
+    g["stats"].zero_()
+
+
+def cpu_baseline(w, host_buf, g, budget_s=15.0):
+    """The oracle as it stands, single-threaded, on the same workload from the
+    same initial state, for as many steps as fit in about budget_s seconds."""
+    from oracle import OracleState, oracle_resolve
+    host = host_buf.numpy((w.host_pool_rows, w.row_bytes))
+    ost = OracleState(R=w.R, S=w.S, L=w.L, row_bytes=w.row_bytes, dev_pool_rows=w.dev_pool_rows)
+    ost.slot_tokens[:], ost.lru_slots[:], ost.lru_clock[:] = g["st0"], g["lru0"], g["clk0"]
+    if len(g["pre_dst"]):
+        ost.dev_pools[0][g["pre_dst"]] = host[g["pre_src"]]
+    rows = 0
+    t_total = 0.0
+    steps = 0
+    for step in range(w.steps):
+        t0 = time.perf_counter()
+        oracle_resolve(ost, page_size=w.P, max_seq_len=w.max_seq_len,
+                       resident_pages=w.resident_pages, req_idx=w.req_idx,
+                       top_k_tokens=w.top_k[step], seq_lens=w.seq_lens[step],
+                       host_cache_locs=w.host_cache_locs, block_table=w.block_table,
+                       host_pools=[host], host_pool_rows=[w.host_pool_rows])
+        t_total += time.perf_counter() - t0
+        rows += w.valid_entries(step)
+        steps += 1
+        if t_total >= budget_s:
+            break
+    return {"value": rows / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of the %d decode steps of the same workload, all %d batch rows, "
+                      "single-threaded C oracle including its row copies (%.2f s, %.1f ms/step)"
+                      % (steps, w.steps, w.B, t_total, 1e3 * t_total / steps)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=10)
+    ap.add_argument("--profile-steps", action="store_true",
+                    help="only run warmup+steps (for rocprofv3); no side measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the resolver shards by request with no "
+              "exchange, so a multi-GPU figure is N independent copies of this one; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hierarchical_sparse_attention_hisparse_amd as hs
+    from workloads import config2_dsa_decode, fill_host_rows_uniform
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    total_steps = args.warmup + args.steps
+    log("generating workload (%d steps)" % total_steps)
+    w = config2_dsa_decode(steps=total_steps)
+    log("host pool %.2f GB pinned" % (w.host_pool_rows * ROW_BYTES / 1e9))
+    host_buf = hs.HostBuffer(w.host_pool_rows * ROW_BYTES)
+    fill_host_rows_uniform(host_buf.torch((w.host_pool_rows, ROW_BYTES)), seed=200,
+                           gen_device="cuda")
+    g = setup_gpu(w, torch, hs, host_buf)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        """One decode step.  Without events it is the single fused entry
+        point; with events the same two kernels are enqueued through the
+        split entry points with an event between them."""
+        if ev is None:
+            hs.hisparse_resolve(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i], g["seq"][i],
+                                g["locs"], None, g["st"], g["lru"], g["clk"], g["out"], g["stats"])
+            return
+        ev[0].record(stream)
+        hs.hisparse_resolve_plan(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i],
+                                 g["seq"][i], g["locs"], None, g["st"], g["lru"], g["clk"],
+                                 g["out"], g["stats"])
+        ev[1].record(stream)
+        hs.hisparse_gather_copy(g["pool"], stream, w.B, 0, w.L, g["stats"])
+        ev[2].record(stream)
+
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stats_before = g["stats"].cpu().numpy().astype(np.uint64)
+    snap = (g["st"].clone(), g["lru"].clone(), g["clk"].clone())
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for j in range(args.steps):
+        step(args.warmup + j)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    stats_after = g["stats"].cpu().numpy().astype(np.uint64)
+    if args.profile_steps:
+        log("timed %.3f ms over %d steps" % (total_ms, args.steps))
+        return
+
+    # Per-kernel durations: the same steps again from the same state, with an
+    # event before, between and after the two kernels of every step.
+    log("per-kernel timing replay of the %d steps" % args.steps)
+    g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    torch.cuda.synchronize()
+    d = (stats_after - stats_before).astype(np.int64)
+    hits, misses, resident, fast, trips = [int(x) for x in d]
+    rows = sum(w.valid_entries(args.warmup + j) for j in range(args.steps))
+    assert rows == hits + misses + resident + fast, (rows, d)
+    long_rows = sum(int(((w.top_k[args.warmup + j] >= 0) &
+                         (w.seq_lens[args.warmup + j][:, None] > w.S)).sum())
+                    for j in range(args.steps))
+    plan_ms = np.array([evs[j][0].elapsed_time(evs[j][1]) for j in range(args.steps)])
+    copy_ms = np.array([evs[j][1].elapsed_time(evs[j][2]) for j in range(args.steps)])
+    value = rows / (total_ms * 1e-3)
+
+    # algorithmic bytes (what the method must move), per launch
+    miss_bytes = misses * ROW_BYTES * w.L / args.steps          # host link, per copy launch
+    n_long = int((w.seq_lens[args.warmup] > w.S).sum())
+    n_fast = w.B - n_long
+    # long rows read top-k + slot map + stamps and write row IDs; every touched
+    # slot gets a stamp, every miss reads its host location and writes the map;
+    # fast-path rows read top-k and write row ID + map + stamp per entry.
+    per_step = lambda x: x / args.steps
+    plan_bytes = (n_long * (8 * w.k + 8 * w.S) + per_step(4 * (hits + misses) + 12 * misses)
+                  + n_fast * 4 * w.k + per_step(12 * fast) + w.B * 16)
+    copy_gbs = miss_bytes / (copy_ms.mean() * 1e-3) / 1e9
+    plan_gbs = plan_bytes / (plan_ms.mean() * 1e-3) / 1e9
+    traffic_copy = load_traffic("gather_copy")
+    traffic_plan = load_traffic("resolve")
+
+    # side measurements (not in the timed region)
+    log("measuring H2D memcpy peak")
+    h2d = measure_h2d_peak(torch)
+    cold = []
+    if args.cold_reps > 0:
+        log("cold step 0 x %d from reset state" % args.cold_reps)
+        for _ in range(args.cold_reps):
+            reset_state(g)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(0, ev)
+            torch.cuda.synchronize()
+            m0 = int(g["stats"][1].item())
+            cold.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), m0))
+    cold_copy_ms = float(np.median([c[1] for c in cold])) if cold else None
+    cold_misses = cold[0][2] if cold else 0
+    cold_gbs = cold_misses * ROW_BYTES * w.L / (cold_copy_ms * 1e-3) / 1e9 if cold else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, host_buf, g)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {
+            "workload": "dsa_decode: 64 requests seq_len U[32768,131072] + 8 fast-path requests "
+                        "seq_len U[1024,4032], top-k 2048, 4096 hot slots, 656-B rows, "
+                        "90% kept / 5% newest-2048 / 5% uniform per step, seq_len +1 per step",
+            "batch_rows": w.B, "long_rows": n_long, "top_k": w.k, "slots": w.S,
+            "row_bytes": ROW_BYTES, "layers": w.L, "steps_timed": args.steps,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "gather_copy (miss rows, pinned host -> HBM)",
+            "bound": "host_link",
+            "achieved": copy_gbs,
+            "peak": HOST_LINK_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": copy_gbs / HOST_LINK_PEAK_GBS,
+            "traffic": (traffic_copy["fetch_bytes_per_launch"] + traffic_copy["write_bytes_per_launch"])
+                       if traffic_copy else None,
+            "measured_peak_h2d_memcpy": h2d,
+            "frac_of_measured_peak": copy_gbs / h2d,
+            "algorithmic_bytes_per_launch": miss_bytes,
+            "avg_launch_ms": float(copy_ms.mean()),
+        },
+        "roofline_plan": {
+            "kernel": "resolve (hit detection, LRU, plan)",
+            "bound": "hbm",
+            "achieved": plan_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": plan_gbs / HBM_PEAK_GBS,
+            "traffic": (traffic_plan["fetch_bytes_per_launch"] + traffic_plan["write_bytes_per_launch"])
+                       if traffic_plan else None,
+            "algorithmic_bytes_per_launch": plan_bytes,
+            "avg_launch_ms": float(plan_ms.mean()),
+        },
+        "detail": {
+            "rows_resolved_per_step": rows / args.steps,
+            "long_row_entries_per_s": long_rows / (total_ms * 1e-3),
+            "hits": hits, "misses": misses, "resident_hits": resident, "fast_path": fast,
+            "tripwires": trips,
+            "hit_rate_long_rows": hits / max(1, hits + misses),
+            "miss_copy_bytes_per_step": miss_bytes,
+            "cold_step0_misses": cold_misses,
+            "cold_step0_copy_ms": cold_copy_ms,
+            "cold_step0_copy_gbs": cold_gbs,
+            "cold_step0_frac_of_measured_peak": (cold_gbs / h2d) if cold else None,
+            "cold_step0_plan_ms": float(np.median([c[0] for c in cold])) if cold else None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    hs.hisparse_destroy_pool(g["pool"])
+    host_buf.free()
+
+
+if __name__ == "__main__":
+    main()

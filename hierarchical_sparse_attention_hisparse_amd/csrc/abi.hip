@@ -31,7 +31,6 @@ struct hisparse_pool {
   float* dec_part_o;            // decode split partials (allocated lazily per shape)
   float* dec_part_ml;
   size_t dec_part_bytes;
-  int copy_chunks;
 };
 
 namespace {
@@ -129,6 +128,12 @@ int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   return HISPARSE_OK;
 }
 
+// Workgroups per batch row of the copy: about 4096 wavefronts in total.
+int copy_chunks_for(int batch) {
+  int c = 4096 / (4 * (batch > 0 ? batch : 1));
+  return c < 4 ? 4 : (c > 64 ? 64 : c);
+}
+
 int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t lb, int32_t le,
                 uint64_t* stats) {
   CopyParams c;
@@ -141,7 +146,7 @@ int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   c.stats = (unsigned long long*)stats;
   c.plan_stride = pool->cfg.max_top_k;
   c.units = pool->cfg.row_bytes / 16;
-  c.chunks = pool->copy_chunks;
+  c.chunks = copy_chunks_for(batch);
   c.layer_begin = lb;
   hipError_t e = launch_gather_copy(c, batch, le - lb, stream);
   if (e != hipSuccess) return hip_fail(e, "gather copy kernel launch");
@@ -199,6 +204,10 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   if (device_pool_rows < need_rows || device_pool_rows > INT32_MAX)
     return fail(HISPARSE_EINVAL, "device_pool_rows %lld must be >= R*S + resident_pages*P = %lld and < 2^31",
                 (long long)device_pool_rows, (long long)need_rows);
+  if (resolve_slots_per_thread(c.slots) > kMaxSlotsPerThread ||
+      resolve_entries_per_thread(c.max_top_k) > kMaxEntriesPerThread)
+    return fail(HISPARSE_EUNSUPPORTED, "slots %d / max_top_k %d exceed the resolver's per-thread limits",
+                c.slots, c.max_top_k);
   const ResolveLds lay = resolve_lds_layout(c.slots, c.max_top_k);
   if (lay.total > kLdsBudget)
     return fail(HISPARSE_EUNSUPPORTED, "slots %d with max_top_k %d need %zu bytes of LDS (> %zu)",
@@ -253,7 +262,6 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   pool->device_pool_rows = device_pool_rows;
   pool->max_pages = c.page_size > 0 ? (c.max_seq_len + c.page_size - 1) / c.page_size : 0;
   pool->dev_ptrs = ddev;
-  pool->copy_chunks = 16;
 
   const size_t entries = (size_t)c.max_batch * c.max_top_k;
   const size_t bytes_src = entries * 8, bytes_dst = entries * 4, bytes_cnt = (size_t)c.max_batch * 4;

@@ -10,7 +10,14 @@ namespace hisparse {
 constexpr int kWave = 64;
 
 // Launch shapes and LDS limits of the resolver.
-constexpr int kResolveThreads = 1024;                 // 16 waves per request row
+#ifndef HISPARSE_RESOLVE_THREADS
+#define HISPARSE_RESOLVE_THREADS 1024
+#endif
+#ifndef HISPARSE_HASH_FACTOR
+#define HISPARSE_HASH_FACTOR 4
+#endif
+constexpr int kResolveThreads = HISPARSE_RESOLVE_THREADS;  // threads per request row
+constexpr int kHashFactor = HISPARSE_HASH_FACTOR;          // table cells per top-k entry
 constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxSlots = 16384;
@@ -34,40 +41,58 @@ __host__ __device__ inline int ilog2(int v) {
 }
 
 // Byte offsets of the resolver's dynamic LDS carve-up for S slots and top-k k.
+// The open-addressing table and the per-entry hit slots are dead once the
+// misses are listed, so the fallback victim sort reuses their bytes.
+constexpr int kResolveScratchInts = 160 + 32 * kVictimRounds;
+
 struct ResolveLds {
-  int hash_size;   // open-addressing table size (power of two >= 2k)
+  int hash_size;   // cells of the open-addressing table (power of two >= 2k)
   int sort_size;   // power of two >= S (fallback sort)
-  size_t off_tok, off_stamp, off_flag, off_etok, off_mentry, off_victim;
-  size_t off_region, off_hkey, off_hval, off_ehit, off_sort, off_scratch;
+  size_t off_hash, off_ehit, off_sort;
+  size_t off_etok, off_mentry, off_victim, off_flag, off_scratch;
   size_t total;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
-__host__ __device__ inline ResolveLds resolve_lds_layout(int S, int k) {
+// Layout for one table size (cells per top-k entry = factor).
+__host__ __device__ inline ResolveLds resolve_lds_layout_f(int S, int k, int factor) {
   ResolveLds L;
-  L.hash_size = next_pow2(2 * k < 64 ? 64 : 2 * k);
+  L.hash_size = next_pow2(factor * k < 64 ? 64 : factor * k);
   L.sort_size = next_pow2(S);
   size_t o = 0;
-  L.off_tok = o;    o = align16(o + 4 * (size_t)S);
-  L.off_stamp = o;  o = align16(o + 4 * (size_t)S);
-  L.off_flag = o;   o = align16(o + (size_t)S);
-  L.off_etok = o;   o = align16(o + 4 * (size_t)k);
-  L.off_mentry = o; o = align16(o + 4 * (size_t)k);
-  L.off_victim = o; o = align16(o + 4 * (size_t)k);
-  // Region used first by the hash table and per-entry hit slots, later (only
-  // if needed) by the fallback sort of victim keys.
-  L.off_region = o;
-  L.off_hkey = o;
-  L.off_hval = align16(L.off_hkey + 4 * (size_t)L.hash_size);
-  L.off_ehit = align16(L.off_hval + 4 * (size_t)L.hash_size);
-  size_t end_hash = align16(L.off_ehit + 4 * (size_t)k);
+  L.off_hash = o;
+  L.off_ehit = align16(L.off_hash + 8 * (size_t)L.hash_size);
+  const size_t end_hash = align16(L.off_ehit + 4 * (size_t)k);
   L.off_sort = o;
-  size_t end_sort = align16(L.off_sort + 8 * (size_t)L.sort_size);
+  const size_t end_sort = align16(L.off_sort + 8 * (size_t)L.sort_size);
   o = end_hash > end_sort ? end_hash : end_sort;
-  L.off_scratch = o; o = align16(o + 8 * (size_t)kResolveWaves * 2);
+  L.off_etok = o;    o = align16(o + 4 * (size_t)k);
+  L.off_mentry = o;  o = align16(o + 4 * (size_t)k);
+  L.off_victim = o;  o = align16(o + 4 * (size_t)k);
+  L.off_flag = o;    o = align16(o + (size_t)S);
+  L.off_scratch = o; o = align16(o + 4 * (size_t)kResolveScratchInts);
   L.total = o;
   return L;
 }
+
+// The sparsest table (kHashFactor cells per entry, down to 2) that fits.
+inline ResolveLds resolve_lds_layout(int S, int k) {
+  ResolveLds L = resolve_lds_layout_f(S, k, kHashFactor);
+  for (int f = kHashFactor / 2; L.total > kLdsBudget && f >= 2; f /= 2) L = resolve_lds_layout_f(S, k, f);
+  return L;
+}
+
+// Items per thread of the resolver (powers of two).
+inline int resolve_slots_per_thread(int S) {
+  const int v = (S + kResolveThreads - 1) / kResolveThreads;
+  return next_pow2(v < 1 ? 1 : v);
+}
+inline int resolve_entries_per_thread(int k) {
+  const int v = (k + kResolveThreads - 1) / kResolveThreads;
+  return next_pow2(v < 1 ? 1 : v);
+}
+constexpr int kMaxSlotsPerThread = 16;
+constexpr int kMaxEntriesPerThread = 8;
 
 }  // namespace hisparse

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace hisparse {
 
 struct ResolveParams {
@@ -23,6 +25,7 @@ struct ResolveParams {
   int32_t* plan_dst;
   int32_t* plan_cnt;
   int32_t plan_stride;
+  ResolveLds lds;  // LDS carve-up for (S, k), filled in by launch_resolve
 };
 
 struct CopyParams {
@@ -55,7 +58,7 @@ struct DecodeParams {
 };
 
 hipError_t prepare_resolve(size_t lds_bytes);
-hipError_t launch_resolve(const ResolveParams& p, int batch, hipStream_t stream);
+hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream);
 hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream);
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
 

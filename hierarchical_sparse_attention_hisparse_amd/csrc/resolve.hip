@@ -1,100 +1,135 @@
 // resolve.hip -- the resolver's plan kernel for gfx950.
 //
-// One workgroup of 1024 threads (16 wavefronts) per batch row.  For one
-// request it performs, in LDS:
-//   1. validity + resident short-circuit, then hashing of the remaining
-//      positions into an open-addressing table (position -> top-k index);
-//   2. one pass over the request's S slots (slot_tokens and stamps staged in
-//      LDS) that probes the table: a slot holding a wanted position is a hit;
-//   3. hit row IDs and stamp refreshes, and a block-wide exclusive scan that
-//      lists the misses in ascending top-k index;
-//   4. victim ranking over the non-hit slots by the key (occupied, stamp,
-//      slot): repeated block-wide minimum extraction with a stable (slot
-//      order) prefix-sum rank inside each key value, and a bitonic sort of
-//      the remaining candidates if a few rounds do not cover all misses;
-//   5. the j-th miss takes the j-th victim: new token, stamp, row ID, and one
+// One workgroup of 1024 threads (16 wavefronts) per batch row.  Thread t owns
+// a contiguous run of SPT slots and a contiguous run of KPT top-k entries, so
+// "ascending slot" and "ascending top-k index" are thread order and every
+// rank below is a block-wide exclusive scan.  Slot tokens and stamps stay in
+// registers; LDS holds an open-addressing table of the pending positions
+// (one 64-bit word per cell: position << 32 | top-k index), the per-entry hit
+// slot, the miss and victim lists, and per-wave partials.  Steps:
+//   1. validity and the resident short-circuit; pending positions are
+//      inserted into the table;
+//   2. each slot holding a pending position marks that entry's hit slot (the
+//      lowest slot if the map was corrupted into duplicates);
+//   3. hits get their row ID and a refreshed stamp; misses are listed in
+//      ascending top-k index;
+//   4. victims: rounds of block-wide minimum over the candidates' (occupied,
+//      stamp) keys, each round taking the slots of the minimum key in slot
+//      order; if a few rounds do not cover every miss, a bitonic LDS sort of
+//      the remaining candidates finishes the ranking;
+//   5. the j-th miss takes the j-th victim: token, stamp, row ID and one
 //      (host row, device row) entry of the compact miss plan.
-// The resolution order and phases follow "vLLM HiSparse 本地 KV 卸载架构"
-// (hot-row lookup and LRU) and "vLLM Hybrid HiSparse 源码实现分析" section
-// 7.2; the fast path (seq_len <= S: slot == position, nothing moves) follows
-// the per-step flow of the gogongxt.com HiSparse page.
+// Resolution order and phases: "vLLM HiSparse 本地 KV 卸载架构" (hot-row lookup
+// and LRU) and "vLLM Hybrid HiSparse 源码实现分析" section 7.2; fast path
+// (seq_len <= S: slot == position, nothing moves): the per-step flow of the
+// gogongxt.com HiSparse page.
 #include <limits.h>
 
 #include "common.h"
 #include "kernels.h"
 
+// Wavefront reductions of the ROCm device library (DPP based).
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_min_u64(
+    unsigned long long);
+extern "C" __device__ __attribute__((const)) int __ockl_wfred_add_i32(int);
+
 namespace hisparse {
 
 namespace {
 
-__device__ inline int block_exscan(int v, int* s_wave, int* total) {
-  const int ln = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int x = v;
+constexpr uint64_t kEmptyCell = ~0ull;
+
+__device__ inline int lane_prefix(uint64_t m) {  // popcount of m below this lane
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Block-wide exclusive prefix sum of small per-thread counts (< 2^BITS) in
+// thread order, with one barrier.  `buf` holds 16 ints used by this call
+// site only.
+template <int BITS>
+__device__ inline int block_exscan_small(int c, int* buf, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  int pre = 0, wt = 0;
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (ln >= d) x += y;
+  for (int q = 0; q < BITS; ++q) {
+    const uint64_t m = __ballot((c >> q) & 1);
+    pre += lane_prefix(m) << q;
+    wt += __popcll(m) << q;
   }
-  if (ln == kWave - 1) s_wave[w] = x;
+  if (lane == 0) buf[wid] = wt;
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kResolveWaves; ++i) {
-    const int t = s_wave[i];
-    base += (i < w) ? t : 0;
-    tot += t;
+  for (int w = 0; w < kResolveWaves; ++w) {
+    const int v = buf[w];
+    base += (w < wid) ? v : 0;
+    tot += v;
   }
-  __syncthreads();
   *total = tot;
-  return base + x - v;
+  return base + pre;
 }
 
-__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_red) {
-  const int ln = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) {
-    const uint64_t o = __shfl_xor(v, d, kWave);
-    v = o < v ? o : v;
-  }
-  if (ln == 0) s_red[w] = v;
+// Block-wide minimum with one barrier; `buf` holds 16 u64 for this call site.
+__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* buf) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const uint64_t wm = __ockl_wfred_min_u64(v);
+  if (lane == 0) buf[wid] = wm;
   __syncthreads();
-  uint64_t m = s_red[0];
+  uint64_t m = buf[0];
 #pragma unroll
-  for (int i = 1; i < kResolveWaves; ++i) {
-    const uint64_t t = s_red[i];
-    m = t < m ? t : m;
+  for (int w = 1; w < kResolveWaves; ++w) {
+    const uint64_t x = buf[w];
+    m = x < m ? x : m;
   }
-  __syncthreads();
   return m;
-}
-
-__device__ inline int wave_sum(int v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
-
-// Victim key of a slot without its slot index: (occupied, stamp) with the
-// signed stamp mapped to an order-preserving unsigned value.
-__device__ inline uint64_t key33(const int32_t* s_tok, const int32_t* s_stamp, int s) {
-  const uint64_t occ = s_tok[s] >= 0 ? 1ull : 0ull;
-  return (occ << 32) | (uint64_t)((uint32_t)s_stamp[s] ^ 0x80000000u);
 }
 
 __device__ inline uint32_t hash_pos(int t, int shift) {
   return ((uint32_t)t * 2654435761u) >> shift;  // Knuth multiplicative hash
 }
 
+constexpr int bits_for(int v) { return v <= 1 ? 1 : 1 + bits_for(v >> 1); }
+
+// Scratch buffers (16 entries each) of the call sites, in ints.
+enum : int {
+  kScrFast = 0,
+  kScrMiss = 16,
+  kScrStats = 32,        // 3 x 16
+  kScrRoundScan = 80,    // kVictimRounds x 16
+  kScrRoundMin = 160,    // kVictimRounds x 16 u64 (= 32 ints each), 8-byte aligned
+  kScrInts = 160 + 32 * kVictimRounds
+};
+static_assert(kScrInts == kResolveScratchInts, "scratch layout");
+
+template <int SPT, int KPT>
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
   const int k = p.k, S = p.S;
   int32_t* outb = p.out + (int64_t)b * k;
   const int32_t* tk = p.topk + (int64_t)b * k;
   const int r = p.req_idx[b];
+  const int nraw = p.seq_lens[b];
+
+  // This thread's top-k entries, loaded before anything depends on r.  The
+  // loads use clamped (always in-range) indices so that they issue back to
+  // back without per-load branches; out-of-range lanes discard the value.
+  const int i0 = tid * KPT;
+  // Lanes past k hold a copy of entry k-1 and are skipped wherever used.
+  int tr[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) tr[j] = -1;
+  if (k > 0) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) tr[j] = tk[min(i0 + j, k - 1)];
+  }
 
   if (r < 0 || r >= p.R) {  // padding row
-    for (int i = tid; i < k; i += kResolveThreads) outb[i] = -1;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (i0 + j < k) outb[i0 + j] = -1;
     if (tid == 0) {
       p.plan_cnt[b] = 0;
       if (r >= p.R && p.stats) atomicAdd(&p.stats[4], 1ull);
@@ -102,19 +137,21 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     return;
   }
 
-  const int nraw = p.seq_lens[b];
   const int64_t n = (int64_t)nraw < p.max_seq_len ? (int64_t)nraw : p.max_seq_len;
   const int32_t c = (int32_t)((uint32_t)p.clk[r] + 1u);
   int32_t* st = p.st + (int64_t)r * S;
   int32_t* lru = p.lru + (int64_t)r * S;
   const int rowbase = r * S;
-  const ResolveLds L = resolve_lds_layout(S, k);
-  int* s_scr = (int*)(smem + L.off_scratch);
+  const ResolveLds& L = p.lds;
+  int* scr = (int*)(smem + L.off_scratch);
 
   if (nraw <= S) {  // fast path: slot == position, nothing copied
     int cnt = 0;
-    for (int i = tid; i < k; i += kResolveThreads) {
-      const int t = tk[i];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = i0 + j;
+      if (i >= k) continue;
+      const int t = tr[j];
       if (t >= 0 && (int64_t)t < n) {
         outb[i] = rowbase + t;
         st[t] = t;
@@ -125,7 +162,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       }
     }
     int tot;
-    block_exscan(cnt, s_scr, &tot);
+    block_exscan_small<bits_for(KPT)>(cnt, scr + kScrFast, &tot);
     if (tid == 0) {
       p.clk[r] = c;
       p.plan_cnt[b] = 0;
@@ -134,94 +171,120 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     return;
   }
 
-  int32_t* s_tok = (int32_t*)(smem + L.off_tok);
-  int32_t* s_stamp = (int32_t*)(smem + L.off_stamp);
-  uint8_t* s_flag = (uint8_t*)(smem + L.off_flag);  // 0 candidate, 1 hit, 2 victim
-  int32_t* e_tok = (int32_t*)(smem + L.off_etok);   // pending position or -1
+  // Slot state of this thread's slots (registers); slots past S hold a copy
+  // of slot S-1 and are excluded wherever used.
+  const int s0 = tid * SPT;
+  int sr[SPT], lr[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = min(s0 + j, S - 1);
+    sr[j] = st[s];
+    lr[j] = lru[s];
+  }
+
+  uint64_t* H = (uint64_t*)(smem + L.off_hash);
+  int32_t* e_hit = (int32_t*)(smem + L.off_ehit);
+  int32_t* e_tok = (int32_t*)(smem + L.off_etok);
   int32_t* m_entry = (int32_t*)(smem + L.off_mentry);
   int32_t* victim = (int32_t*)(smem + L.off_victim);
-  int32_t* h_key = (int32_t*)(smem + L.off_hkey);
-  int32_t* h_val = (int32_t*)(smem + L.off_hval);
-  int32_t* e_hit = (int32_t*)(smem + L.off_ehit);
+  uint8_t* s_flag = (uint8_t*)(smem + L.off_flag);
   uint64_t* s_sort = (uint64_t*)(smem + L.off_sort);
-  const int H = L.hash_size;
-  const int hshift = 32 - ilog2(H);
+  const int HS = L.hash_size;
+  const int hshift = 32 - ilog2(HS);
 
-  for (int i = tid; i < H; i += kResolveThreads) {
-    h_key[i] = -1;
-    h_val[i] = INT_MAX;
-  }
-  for (int i = tid; i < k; i += kResolveThreads) e_hit[i] = INT_MAX;
-  for (int s = tid; s < S; s += kResolveThreads) {  // stage the slot state
-    s_tok[s] = st[s];
-    s_stamp[s] = lru[s];
-    s_flag[s] = 0;
-  }
+  for (int x = tid; x < HS; x += kResolveThreads) H[x] = kEmptyCell;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (i0 + j < k) e_hit[i0 + j] = INT_MAX;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if (s0 + j < S) s_flag[s0 + j] = 0;
   __syncthreads();
 
-  // Step 1: validity, resident pages, hash of the positions still pending.
+  // Step 1: validity, resident pages, table of pending positions.
   int n_res = 0, n_trip = 0;
-  for (int i = tid; i < k; i += kResolveThreads) {
-    const int t = tk[i];
-    int pend = -1;
-    if (t >= 0 && (int64_t)t < n) {
-      bool resident = false;
-      if (p.bt != nullptr) {
-        const int pg = p.bt[(int64_t)r * p.max_pages + t / p.P];
-        if (pg >= 0 && (int64_t)pg < p.resident_pages) {
-          outb[i] = (int)((int64_t)p.R * S + (int64_t)pg * p.P + t % p.P);
-          resident = true;
-          ++n_res;
-        } else if (pg >= 0) {
-          ++n_trip;
-        }
-      }
-      if (!resident) {
-        pend = t;
-        uint32_t h = hash_pos(t, hshift);
-        while (true) {
-          const int prev = atomicCAS(&h_key[h], -1, t);
-          if (prev == -1 || prev == t) {
-            atomicMin(&h_val[h], i);
-            break;
-          }
-          h = (h + 1) & (H - 1);
-        }
-      }
-    } else {
+  unsigned pend = 0;
+  int pgs[KPT];
+  if (p.bt != nullptr) {  // all block-table loads first, at in-range indices
+    const int32_t* btr = p.bt + (int64_t)r * p.max_pages;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int t = tr[j];
+      const bool v = t >= 0 && (int64_t)t < n;
+      pgs[j] = btr[v ? t / p.P : 0];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = i0 + j;
+    if (i >= k) continue;
+    const int t = tr[j];
+    if (t < 0 || (int64_t)t >= n) {
       outb[i] = -1;
+      continue;
     }
-    e_tok[i] = pend;
-  }
-  __syncthreads();
-
-  // Step 2: each slot holding a pending position marks that entry's hit slot
-  // (the lowest such slot if the map were ever corrupted into duplicates).
-  const int seg = (S + kResolveThreads - 1) / kResolveThreads;
-  const int s0 = min(S, tid * seg), s1 = min(S, s0 + seg);
-  for (int s = tid; s < S; s += kResolveThreads) {
-    const int tok = s_tok[s];
-    if (tok >= 0 && (int64_t)tok < n) {
-      uint32_t h = hash_pos(tok, hshift);
-      while (true) {
-        const int key = h_key[h];
-        if (key == tok) {
-          atomicMin(&e_hit[h_val[h]], s);
-          break;
-        }
-        if (key == -1) break;
-        h = (h + 1) & (H - 1);
+    if (p.bt != nullptr) {
+      const int pg = pgs[j];
+      if (pg >= 0 && (int64_t)pg < p.resident_pages) {
+        outb[i] = (int)((int64_t)p.R * S + (int64_t)pg * p.P + t % p.P);
+        ++n_res;
+        continue;
       }
+      if (pg >= 0) ++n_trip;
+    }
+    pend |= 1u << j;
+    e_tok[i] = t;
+    const uint64_t cell = ((uint64_t)(uint32_t)t << 32) | (uint32_t)i;
+    uint32_t h = hash_pos(t, hshift);
+    while (true) {
+      const uint64_t prev = atomicCAS((unsigned long long*)&H[h], kEmptyCell, cell);
+      if (prev == kEmptyCell || (int)(prev >> 32) == t) break;  // inserted, or a repeat
+      h = (h + 1) & (HS - 1);
     }
   }
   __syncthreads();
 
-  // Step 3: hits (row ID, stamp refresh) and the misses in ascending index.
-  const int segk = (k + kResolveThreads - 1) / kResolveThreads;
-  const int i0 = min(k, tid * segk), i1 = min(k, i0 + segk);
+  // Step 2: probe the table with every slot's token; the SPT probes of a
+  // thread advance together so a wavefront waits for its longest chain once.
+  {
+    uint32_t hh[SPT];
+    uint64_t hv[SPT];
+    unsigned live = 0;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int tok = sr[j];
+      const bool ok = (s0 + j < S) && tok >= 0 && (int64_t)tok < n;
+      hh[j] = hash_pos(tok, hshift);
+      hv[j] = ok ? H[hh[j]] : kEmptyCell;
+      if (ok) live |= 1u << j;
+    }
+    while (true) {
+      unsigned next = 0;
+#pragma unroll
+      for (int j = 0; j < SPT; ++j)
+        if ((live & (1u << j)) && hv[j] != kEmptyCell && (int)(hv[j] >> 32) != sr[j])
+          next |= 1u << j;
+      if (next == 0) break;
+#pragma unroll
+      for (int j = 0; j < SPT; ++j)
+        if (next & (1u << j)) {
+          hh[j] = (hh[j] + 1) & (HS - 1);
+          hv[j] = H[hh[j]];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if ((live & (1u << j)) && hv[j] != kEmptyCell) atomicMin(&e_hit[(int)(uint32_t)hv[j]], s0 + j);
+  }
+  __syncthreads();
+
+  // Step 3: hits and the ordered miss list.
   int n_hit = 0, my_miss = 0;
-  for (int i = i0; i < i1; ++i) {
-    if (e_tok[i] < 0) continue;
+  unsigned missbits = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (!(pend & (1u << j))) continue;
+    const int i = i0 + j;
     const int s = e_hit[i];
     if (s != INT_MAX) {
       outb[i] = rowbase + s;
@@ -229,34 +292,55 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       s_flag[s] = 1;
       ++n_hit;
     } else {
+      missbits |= 1u << j;
       ++my_miss;
     }
   }
+  {
+    const int a0 = __ockl_wfred_add_i32(n_hit);
+    const int a1 = __ockl_wfred_add_i32(n_res);
+    const int a2 = __ockl_wfred_add_i32(n_trip);
+    if (lane == 0) {
+      scr[kScrStats + wid] = a0;
+      scr[kScrStats + 16 + wid] = a1;
+      scr[kScrStats + 32 + wid] = a2;
+    }
+  }
   int m_total;
-  int mpos = block_exscan(my_miss, s_scr, &m_total);
-  for (int i = i0; i < i1; ++i)
-    if (e_tok[i] >= 0 && e_hit[i] == INT_MAX) m_entry[mpos++] = i;
+  int mpos = block_exscan_small<bits_for(KPT)>(my_miss, scr + kScrMiss, &m_total);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (missbits & (1u << j)) m_entry[mpos++] = i0 + j;
 
-  // Step 4: victims = the m_total smallest (occupied, stamp, slot) among
-  // non-hit slots, in that order.  Each round takes the smallest remaining
-  // (occupied, stamp) value and ranks its slots in slot order.
+  // Step 4: victims, in (occupied, stamp, slot) order among non-hit slots.
+  uint64_t key[SPT];
+  unsigned cand = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    key[j] = ((uint64_t)(sr[j] >= 0 ? 1u : 0u) << 32) | (uint64_t)((uint32_t)lr[j] ^ 0x80000000u);
+    if (s0 + j < S && s_flag[s0 + j] == 0) cand |= 1u << j;
+  }
   int need = m_total, vbase = 0;
+#pragma unroll 1
   for (int round = 0; round < kVictimRounds && need > 0; ++round) {
     uint64_t my = ~0ull;
-    for (int s = s0; s < s1; ++s)
-      if (s_flag[s] == 0) {
-        const uint64_t kk = key33(s_tok, s_stamp, s);
-        my = kk < my ? kk : my;
-      }
-    const uint64_t kmin = block_min_u64(my, (uint64_t*)s_scr);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if ((cand & (1u << j)) && key[j] < my) my = key[j];
+    const uint64_t kmin =
+        block_min_u64(my, (uint64_t*)(scr + kScrRoundMin + 32 * round));
     int cnt = 0;
-    for (int s = s0; s < s1; ++s) cnt += (s_flag[s] == 0 && key33(s_tok, s_stamp, s) == kmin);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) cnt += ((cand & (1u << j)) && key[j] == kmin) ? 1 : 0;
     int tot;
-    int pos = block_exscan(cnt, s_scr, &tot);
-    for (int s = s0; s < s1 && pos < need; ++s) {
-      if (s_flag[s] == 0 && key33(s_tok, s_stamp, s) == kmin) {
-        victim[vbase + pos] = s;
-        s_flag[s] = 2;
+    int pos = block_exscan_small<bits_for(SPT)>(cnt, scr + kScrRoundScan + 16 * round, &tot);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      if ((cand & (1u << j)) && key[j] == kmin) {
+        if (pos < need) {
+          victim[vbase + pos] = s0 + j;
+          cand &= ~(1u << j);
+        }
         ++pos;
       }
     }
@@ -264,14 +348,15 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     vbase += take;
     need -= take;
   }
-  if (need > 0) {  // many distinct stamps among the victims: full sort
-    __syncthreads();
+  if (need > 0) {  // many distinct stamps among the victims: sort the rest
     const int N = L.sort_size;
-    for (int x = tid; x < N; x += kResolveThreads) {
-      uint64_t v = ~0ull;
-      if (x < S && s_flag[x] == 0) v = (key33(s_tok, s_stamp, x) << 16) | (uint64_t)x;
-      s_sort[x] = v;
+    __syncthreads();  // the table region is reused for the sort
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int s = s0 + j;
+      if (s < N) s_sort[s] = (cand & (1u << j)) ? ((key[j] << 16) | (uint64_t)s) : ~0ull;
     }
+    for (int x = tid + kResolveThreads * SPT; x < N; x += kResolveThreads) s_sort[x] = ~0ull;
     __syncthreads();
     for (int size = 2; size <= N; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -288,12 +373,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         __syncthreads();
       }
     }
-    for (int j = tid; j < need; j += kResolveThreads)
-      victim[vbase + j] = (int)(s_sort[j] & 0xFFFFull);
+    for (int j = tid; j < need; j += kResolveThreads) {
+      const int s = (int)(s_sort[j] & 0xFFFFull);
+      victim[vbase + j] = s < S ? s : S - 1;  // always < S: candidates >= misses
+    }
   }
   __syncthreads();
 
-  // Step 5: assign the j-th miss to the j-th victim and emit the plan.
+  // Step 5: the j-th miss takes the j-th victim; emit the compact plan.
   int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
   int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
   const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
@@ -309,21 +396,12 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     pdst[j] = row;
   }
 
-  // Counters: one atomic per counter per workgroup.
-  const int w = tid / kWave, ln = tid & (kWave - 1);
-  const int a0 = wave_sum(n_hit), a1 = wave_sum(n_res), a2 = wave_sum(n_trip);
-  if (ln == 0) {
-    s_scr[w] = a0;
-    s_scr[kResolveWaves + w] = a1;
-    s_scr[2 * kResolveWaves + w] = a2;
-  }
-  __syncthreads();
   if (tid == 0) {
-    int h = 0, rs = 0, tr = 0;
-    for (int i = 0; i < kResolveWaves; ++i) {
-      h += s_scr[i];
-      rs += s_scr[kResolveWaves + i];
-      tr += s_scr[2 * kResolveWaves + i];
+    int h = 0, rs = 0, tr2 = 0;
+    for (int w = 0; w < kResolveWaves; ++w) {
+      h += scr[kScrStats + w];
+      rs += scr[kScrStats + 16 + w];
+      tr2 += scr[kScrStats + 32 + w];
     }
     p.plan_cnt[b] = m_total;
     p.clk[r] = c;
@@ -331,23 +409,67 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       if (h) atomicAdd(&p.stats[0], (unsigned long long)h);
       if (m_total) atomicAdd(&p.stats[1], (unsigned long long)m_total);
       if (rs) atomicAdd(&p.stats[2], (unsigned long long)rs);
-      if (tr) atomicAdd(&p.stats[4], (unsigned long long)tr);
+      if (tr2) atomicAdd(&p.stats[4], (unsigned long long)tr2);
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_resolve(const ResolveParams& p, int batch, hipStream_t stream) {
-  if (batch <= 0) return hipSuccess;
-  const ResolveLds L = resolve_lds_layout(p.S, p.k);
-  hipLaunchKernelGGL(resolve_kernel, dim3(batch), dim3(kResolveThreads), L.total, stream, p);
+template <int SPT, int KPT>
+hipError_t launch_t(const ResolveParams& p, int batch, size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((resolve_kernel<SPT, KPT>), dim3(batch), dim3(kResolveThreads), lds, stream,
+                     p);
   return hipGetLastError();
 }
 
-hipError_t prepare_resolve(size_t lds_bytes) {
-  return hipFuncSetAttribute((const void*)resolve_kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+template <int SPT>
+hipError_t launch_k(const ResolveParams& p, int batch, size_t lds, hipStream_t stream, int kpt) {
+  switch (kpt) {
+    case 1: return launch_t<SPT, 1>(p, batch, lds, stream);
+    case 2: return launch_t<SPT, 2>(p, batch, lds, stream);
+    case 4: return launch_t<SPT, 4>(p, batch, lds, stream);
+    default: return launch_t<SPT, 8>(p, batch, lds, stream);
+  }
+}
+
+template <int SPT, int KPT>
+hipError_t set_attr() {
+  return hipFuncSetAttribute((const void*)resolve_kernel<SPT, KPT>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+}
+
+template <int SPT>
+hipError_t set_attr_k() {
+  hipError_t e = set_attr<SPT, 1>();
+  if (e == hipSuccess) e = set_attr<SPT, 2>();
+  if (e == hipSuccess) e = set_attr<SPT, 4>();
+  if (e == hipSuccess) e = set_attr<SPT, 8>();
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  p.lds = resolve_lds_layout(p.S, p.k);
+  const size_t lds = p.lds.total;
+  const int spt = resolve_slots_per_thread(p.S);
+  const int kpt = resolve_entries_per_thread(p.k);
+  switch (spt) {
+    case 1: return launch_k<1>(p, batch, lds, stream, kpt);
+    case 2: return launch_k<2>(p, batch, lds, stream, kpt);
+    case 4: return launch_k<4>(p, batch, lds, stream, kpt);
+    case 8: return launch_k<8>(p, batch, lds, stream, kpt);
+    default: return launch_k<16>(p, batch, lds, stream, kpt);
+  }
+}
+
+hipError_t prepare_resolve(size_t) {
+  hipError_t e = set_attr_k<1>();
+  if (e == hipSuccess) e = set_attr_k<2>();
+  if (e == hipSuccess) e = set_attr_k<4>();
+  if (e == hipSuccess) e = set_attr_k<8>();
+  if (e == hipSuccess) e = set_attr_k<16>();
+  return e;
 }
 
 }  // namespace hisparse
