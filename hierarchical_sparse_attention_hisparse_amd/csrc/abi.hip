@@ -28,9 +28,6 @@ struct hisparse_pool {
   int64_t* d_host_rows;         // [L]
   // host copies
   unsigned char** dev_ptrs;     // [L]
-  float* dec_part_o;            // decode split partials (allocated lazily per shape)
-  float* dec_part_ml;
-  size_t dec_part_bytes;
 };
 
 namespace {
@@ -288,6 +285,7 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   if (e == hipSuccess) e = hipMemcpy(pool->d_dev_ptrs, ddev, bytes_tab, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(pool->d_host_rows, host_pool_rows, bytes_tab, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = prepare_resolve(kLdsBudget);
+  if (e == hipSuccess) e = prepare_sparse_mla_decode();
   free(hdev);
   if (e != hipSuccess) {
     (void)hipFree(ws);
@@ -302,7 +300,6 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
 void hisparse_destroy_pool(hisparse_pool* pool) {
   if (!pool) return;
   if (pool->plan_src) (void)hipFree(pool->plan_src);
-  if (pool->dec_part_o) (void)hipFree(pool->dec_part_o);
   free(pool->dev_ptrs);
   free(pool);
 }
@@ -364,10 +361,38 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch,
                                int32_t top_k, int32_t layer, const void* q_bf16,
                                const int32_t* device_buffer_locs, float softmax_scale,
                                void* out_bf16) {
-  (void)stream; (void)q_bf16; (void)device_buffer_locs; (void)softmax_scale; (void)out_bf16;
-  (void)batch; (void)heads; (void)top_k; (void)layer;
   if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
-  return fail(HISPARSE_EUNSUPPORTED, "sparse-MLA decode is not built yet");
+  if (batch < 0) return fail(HISPARSE_EINVAL, "batch %d < 0", batch);
+  if (heads <= 0 || heads % 16 != 0)
+    return fail(HISPARSE_EUNSUPPORTED, "heads %d must be a positive multiple of 16", heads);
+  if (top_k < 0 || top_k > pool->cfg.max_top_k)
+    return fail(HISPARSE_EINVAL, "top_k %d outside [0, max_top_k=%d]", top_k, pool->cfg.max_top_k);
+  if (layer < 0 || layer >= pool->cfg.num_layers)
+    return fail(HISPARSE_EINVAL, "layer %d outside [0, %d)", layer, pool->cfg.num_layers);
+  if (pool->cfg.row_bytes < 656)
+    return fail(HISPARSE_EUNSUPPORTED, "row_bytes %d is smaller than the 656-byte sparse-MLA row",
+                pool->cfg.row_bytes);
+  if (batch == 0) return ok();
+  if (!q_bf16 || !out_bf16 || (top_k > 0 && !device_buffer_locs))
+    return fail(HISPARSE_EINVAL, "q_bf16, out_bf16 and device_buffer_locs must not be NULL");
+  if (!aligned(q_bf16, 16) || !aligned(out_bf16, 8) || !aligned(device_buffer_locs, 4))
+    return fail(HISPARSE_EINVAL, "q_bf16 must be 16-byte, out_bf16 8-byte and locs 4-byte aligned");
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  DecodeParams d;
+  d.pool = pool->dev_ptrs[layer];
+  d.pool_rows = pool->device_pool_rows;
+  d.row_bytes = pool->cfg.row_bytes;
+  d.heads = heads;
+  d.k = top_k;
+  d.batch = batch;
+  d.scale = softmax_scale;
+  d.q = (const uint16_t*)q_bf16;
+  d.locs = device_buffer_locs;
+  d.out = (uint16_t*)out_bf16;
+  hipError_t e = launch_sparse_mla_decode(d, batch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse-MLA decode kernel launch");
+  return ok();
 }
 
 }  // extern "C"

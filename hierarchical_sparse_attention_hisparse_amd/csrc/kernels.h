@@ -48,18 +48,18 @@ struct DecodeParams {
   int32_t row_bytes;
   int32_t heads;
   int32_t k;
+  int32_t batch;
   float scale;
-  const uint16_t* q;     // bf16 bits [B][H][576]
-  const int32_t* locs;   // [B][k]
-  uint16_t* out;         // bf16 bits [B][H][512]
-  float* part_o;         // [B][H/16][splits][16][512] partial outputs
-  float* part_ml;        // [B][H/16][splits][16][2] partial max / sum
-  int32_t splits;
+  const uint16_t* q;     // bf16 bits [batch][heads][576]
+  const int32_t* locs;   // [batch][k]
+  uint16_t* out;         // bf16 bits [batch][heads][512]
 };
 
 hipError_t prepare_resolve(size_t lds_bytes);
 hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream);
 hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream);
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
+hipError_t prepare_sparse_mla_decode();
+size_t decode_lds_bytes();
 
 }  // namespace hisparse

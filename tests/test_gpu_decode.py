@@ -1,0 +1,140 @@
+"""GPU parity of the sparse-MLA decode kernel against the float64 CPU oracle.
+
+Tolerance: for every (batch row, head), max|O_gpu - O_ref| / max|O_ref| must
+not exceed 2e-2 (normwise; the elementwise ratio is meaningless near zero).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hisparse_amd as hs
+from oracle import oracle_sparse_mla_decode
+from tests.harness import Pair, make_host_pools
+from workloads import (config2_dsa_decode, fill_host_rows_mla, make_queries, synth)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+SCALE = 1.0 / math.sqrt(192.0)
+
+
+def _normwise(got, ref):
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return np.where(den > 0, num / np.maximum(den, 1e-30), num)
+
+
+def _run_decode(dev_pool, locs_np, q, heads, max_top_k):
+    B, k = locs_np.shape
+    hb = hs.HostBuffer(656 * 16)
+    cfg = hs.PoolConfig(max_requests=1, slots=max(16, max_top_k), max_top_k=max(1, max_top_k),
+                        max_batch=1, max_seq_len=16)
+    pool = hs.hisparse_init_pool(cfg, [hb], [16], [dev_pool], dev_pool.shape[0])
+    try:
+        locs = torch.from_numpy(locs_np).cuda()
+        out = torch.empty((B, heads, 512), dtype=torch.bfloat16, device="cuda")
+        hs.hisparse_sparse_mla_decode(pool, None, B, heads, k, 0, q, locs, SCALE, out)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64)
+    finally:
+        hs.hisparse_destroy_pool(pool)
+        hb.free()
+
+
+@pytest.mark.parametrize("B,H,k", [(5, 32, 77), (3, 16, 33), (2, 48, 64), (4, 128, 300)])
+def test_decode_small_vs_oracle(B, H, k):
+    print("[decode] B=%d H=%d k=%d" % (B, H, k), flush=True)
+    rows = 900
+    dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 31 + k, gen_device="cuda")
+    rng = np.random.default_rng(k)
+    locs = rng.integers(0, rows, size=(B, k)).astype(np.int32)
+    locs[0, ::7] = -1                      # masked entries
+    locs[-1, 3] = rows + 5                 # out of range: skipped
+    if B > 2:
+        locs[1, :] = -1                    # a row with nothing to attend to
+        locs[1, k // 2] = 11
+    q = make_queries(B, H, seed=k, device="cuda")
+    got = _run_decode(dev, locs, q, H, k)
+    ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16), locs,
+                                   dev.cpu().numpy(), float(np.float32(SCALE)))
+    err = _normwise(got, ref)
+    print("[decode] max normwise error %.3g" % err.max(), flush=True)
+    assert err.max() <= TOL
+
+
+def test_decode_all_invalid_gives_zero():
+    dev = torch.empty((64, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 3, gen_device="cuda")
+    locs = np.full((2, 40), -1, np.int32)
+    q = make_queries(2, 16, seed=1, device="cuda")
+    got = _run_decode(dev, locs, q, 16, 40)
+    assert np.all(got == 0)
+
+
+def test_decode_after_resolver():
+    """Resolver output feeds the decode on the same pool (small DSA-like)."""
+    print("[decode+resolve]", flush=True)
+    w = synth("dec", 41, R=6, S=512, k=256, steps=3, n0=[3000, 2500, 400, 8000, 100, 2000],
+              grow=1, keep=200, recent=20, recent_window=256)
+    bufs = make_host_pools(w, kind="mla")
+    pair = Pair(w, bufs)
+    try:
+        for step in range(w.steps):
+            dst, src = pair.gpu_step(step)
+            pair.oracle_step(step, dst, src)
+        torch.cuda.synchronize()
+        H = 64
+        q = make_queries(w.B, H, seed=5, device="cuda")
+        out = torch.empty((w.B, H, 512), dtype=torch.bfloat16, device="cuda")
+        hs.hisparse_sparse_mla_decode(pair.pool, None, w.B, H, w.k, 0, q, pair.out, SCALE, out)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16),
+                                       pair.out.cpu().numpy(), pair.ost.dev_pools[0],
+                                       float(np.float32(SCALE)))
+        err = _normwise(got, ref)
+        print("[decode+resolve] max normwise error %.3g" % err.max(), flush=True)
+        assert err.max() <= TOL
+    finally:
+        pair.close()
+
+
+def test_config5_full_size_sampled():
+    """Config 5: the DSA-decode resolver output (72 rows, top-2048) feeds
+    128-head decode; rows sampled for the float64 oracle."""
+    print("[config5] generating", flush=True)
+    w = config2_dsa_decode(steps=2)
+    bufs = make_host_pools(w, kind="mla")
+    pair = Pair(w, bufs, with_oracle=False)
+    try:
+        for step in range(w.steps):
+            pair.gpu_step(step)
+        torch.cuda.synchronize()
+        H = 128
+        q = make_queries(w.B, H, seed=55, device="cuda")
+        out = torch.empty((w.B, H, 512), dtype=torch.bfloat16, device="cuda")
+        hs.hisparse_sparse_mla_decode(pair.pool, None, w.B, H, w.k, 0, q, pair.out, SCALE, out)
+        torch.cuda.synchronize()
+        locs = pair.out.cpu().numpy()
+        rng = np.random.default_rng(0)
+        rows = sorted(rng.choice(w.B, size=6, replace=False).tolist())
+        short = [b for b in range(w.B) if w.seq_lens[-1][b] <= w.S][:1]
+        rows = sorted(set(rows + short))
+        used = np.unique(locs[rows][locs[rows] >= 0])
+        pool_rows = pair.dev_pools[0].index_select(0, torch.from_numpy(used.astype(np.int64)).cuda()).cpu().numpy()
+        remap = np.full(w.dev_pool_rows, -1, np.int64)
+        remap[used] = np.arange(len(used))
+        sub_locs = np.where(locs[rows] >= 0, remap[np.maximum(locs[rows], 0)], -1).astype(np.int32)
+        print("[config5] oracle on batch rows %s" % rows, flush=True)
+        ref = oracle_sparse_mla_decode(q[rows].cpu().view(torch.int16).numpy().astype(np.uint16),
+                                       sub_locs, np.ascontiguousarray(pool_rows),
+                                       float(np.float32(SCALE)))
+        got = out[rows].float().cpu().numpy().astype(np.float64)
+        err = _normwise(got, ref)
+        print("[config5] max normwise error %.3g" % err.max(), flush=True)
+        assert err.max() <= TOL
+        assert np.isfinite(out.float().cpu().numpy()).all()
+    finally:
+        pair.close()
