@@ -1,0 +1,60 @@
+"""Bit-exact parity at the full workload sizes, every step.
+
+DSA decode (72 rows, top-2048, 4096 slots, 64 steps) is run through the
+same single fused entry point the benchmark times; mixed residency (128
+requests of 131072 tokens with 16384 resident tail tokens) at 50/90/99 %
+reuse from cold; the 1M-token index-shared case with 4 layers of 11 GB host
+pools each.  Every step compares row IDs, slot map, stamps, clocks,
+counters and the device rows that step names; the pools are compared at
+the end.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.harness import run_parity
+from workloads import config2_dsa_decode, config3_mixed_residency, config4_indexshare_1m
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(name, every=8):
+    def f(step):
+        if step % every == 0:
+            print("[%s] step %d bit-exact" % (name, step), flush=True)
+    return f
+
+
+@pytest.mark.timeout(600)
+def test_config2_dsa_decode_all_steps():
+    print("[config2] generating 72 rows x 64 steps", flush=True)
+    w = config2_dsa_decode()
+    stats = run_parity(w, log=_log("config2"))
+    hits, misses, res, fast, trip = [int(x) for x in stats]
+    print("[config2] stats hits=%d misses=%d fast=%d" % (hits, misses, fast), flush=True)
+    assert fast > 0 and misses > 0 and trip == 0
+    long_hit_rate = hits / (hits + misses)
+    assert long_hit_rate > 0.8       # adjacent-step overlap of ~90 % by construction
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("f", [0.5, 0.9, 0.99])
+def test_config3_mixed_residency(f):
+    print("[config3 f=%g] generating 128 x 131072" % f, flush=True)
+    w = config3_mixed_residency(f)
+    stats = run_parity(w, log=_log("config3 f=%g" % f))
+    hits, misses, res, fast, trip = [int(x) for x in stats]
+    print("[config3 f=%g] hits=%d misses=%d resident=%d" % (f, hits, misses, res), flush=True)
+    assert res > 0 and trip == 0
+    # about 12.5 % of uniform draws land in the resident tail
+    assert 0.05 < res / (hits + misses + res) < 0.25
+
+
+@pytest.mark.timeout(900)
+def test_config4_indexshare_1m_four_layers():
+    print("[config4] generating 16 x 1M tokens, 4 layers (44 GB pinned)", flush=True)
+    w = config4_indexshare_1m()
+    stats = run_parity(w, log=_log("config4", every=4))
+    hits, misses, res, fast, trip = [int(x) for x in stats]
+    print("[config4] hits=%d misses=%d" % (hits, misses), flush=True)
+    assert misses > 0 and hits > 0 and trip == 0
