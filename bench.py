@@ -33,6 +33,8 @@ import numpy as np  # noqa: E402
 METRIC = "top-k rows resolved/s at B=64,k=2048; miss-copy GB/s vs host-link roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 HOST_LINK_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+DECODE_HEADS = 128
 ROW_BYTES = 656
 KERNEL_SOURCES = {
     "gather_copy": "hierarchical_sparse_attention_hisparse_amd/csrc/gather.hip",
@@ -154,7 +156,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=10)
     ap.add_argument("--profile-steps", action="store_true",
-                    help="only run warmup+steps (for rocprofv3); no side measurements")
+                    help="only run warmup+steps and 5 decode calls (for rocprofv3)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 3 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the resolver shards by request with no "
@@ -163,8 +167,19 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        # a plain elementwise kernel that reads 256 MiB and writes 256 MiB
+        # with 16-byte vector accesses
+        src = torch.ones(256 << 20, dtype=torch.int8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("negated 3 x 256 MiB")
+        return
     import hierarchical_sparse_attention_hisparse_amd as hs
-    from workloads import config2_dsa_decode, fill_host_rows_uniform
+    from workloads import config2_dsa_decode, fill_host_rows_mla, make_queries
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -173,8 +188,8 @@ def main():
     w = config2_dsa_decode(steps=total_steps)
     log("host pool %.2f GB pinned" % (w.host_pool_rows * ROW_BYTES / 1e9))
     host_buf = hs.HostBuffer(w.host_pool_rows * ROW_BYTES)
-    fill_host_rows_uniform(host_buf.torch((w.host_pool_rows, ROW_BYTES)), seed=200,
-                           gen_device="cuda")
+    # sparse-MLA rows: fp8 latent with per-128 scales + bf16 rope
+    fill_host_rows_mla(host_buf.torch((w.host_pool_rows, ROW_BYTES)), seed=200, gen_device="cuda")
     g = setup_gpu(w, torch, hs, host_buf)
     stream = torch.cuda.current_stream()
 
@@ -213,18 +228,51 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     stats_after = g["stats"].cpu().numpy().astype(np.uint64)
     if args.profile_steps:
+        q = make_queries(w.B, DECODE_HEADS, seed=55, device="cuda")
+        out = torch.empty((w.B, DECODE_HEADS, 512), dtype=torch.bfloat16, device="cuda")
+        for _ in range(5):
+            hs.hisparse_sparse_mla_decode(g["pool"], stream, w.B, DECODE_HEADS, w.k, 0, q,
+                                          g["out"], 1.0 / math.sqrt(192.0), out)
+        torch.cuda.synchronize()
         log("timed %.3f ms over %d steps" % (total_ms, args.steps))
         return
 
-    # Per-kernel durations: the same steps again from the same state, with an
-    # event before, between and after the two kernels of every step.
+    # Per-kernel durations, from the same state as the timed region:
+    #  - plan: the K plan launches back to back between two events (the plan
+    #    of step j+1 does not read anything the copy of step j writes);
+    #  - copy: after each step's plan, COPY_REPS back-to-back launches of that
+    #    step's copy between two events (re-copying a plan rewrites the same
+    #    bytes), so launch latency is amortised the way it is in the step.
+    COPY_REPS = 4
     log("per-kernel timing replay of the %d steps" % args.steps)
     g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for j in range(args.steps):
+        i = args.warmup + j
+        hs.hisparse_resolve_plan(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i],
+                                 g["seq"][i], g["locs"], None, g["st"], g["lru"], g["clk"],
+                                 g["out"], g["stats"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan_ms = np.array([e0.elapsed_time(e1) / args.steps])
+    g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for j in range(args.steps):
-        step(args.warmup + j, evs[j])
+        i = args.warmup + j
+        hs.hisparse_resolve_plan(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i],
+                                 g["seq"][i], g["locs"], None, g["st"], g["lru"], g["clk"],
+                                 g["out"], g["stats"])
+        cev[j][0].record(stream)
+        for _ in range(COPY_REPS):
+            hs.hisparse_gather_copy(g["pool"], stream, w.B, 0, w.L, None)
+        cev[j][1].record(stream)
     torch.cuda.synchronize()
+    copy_ms = np.array([cev[j][0].elapsed_time(cev[j][1]) / COPY_REPS for j in range(args.steps)])
+
     d = (stats_after - stats_before).astype(np.int64)
     hits, misses, resident, fast, trips = [int(x) for x in d]
     rows = sum(w.valid_entries(args.warmup + j) for j in range(args.steps))
@@ -232,8 +280,6 @@ def main():
     long_rows = sum(int(((w.top_k[args.warmup + j] >= 0) &
                          (w.seq_lens[args.warmup + j][:, None] > w.S)).sum())
                     for j in range(args.steps))
-    plan_ms = np.array([evs[j][0].elapsed_time(evs[j][1]) for j in range(args.steps)])
-    copy_ms = np.array([evs[j][1].elapsed_time(evs[j][2]) for j in range(args.steps)])
     value = rows / (total_ms * 1e-3)
 
     # algorithmic bytes (what the method must move), per launch
@@ -268,6 +314,34 @@ def main():
     cold_copy_ms = float(np.median([c[1] for c in cold])) if cold else None
     cold_misses = cold[0][2] if cold else 0
     cold_gbs = cold_misses * ROW_BYTES * w.L / (cold_copy_ms * 1e-3) / 1e9 if cold else None
+
+    # The decode consumer on the rows of the last timed step (config 5 shape:
+    # 128 heads, 576-dim bf16 queries, softmax scale 1/sqrt(192)).
+    log("sparse-MLA decode consumer")
+    last = args.warmup + args.steps - 1
+    g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+    for j in range(args.steps):
+        step(args.warmup + j)
+    q = make_queries(w.B, DECODE_HEADS, seed=55, device="cuda")
+    out = torch.empty((w.B, DECODE_HEADS, 512), dtype=torch.bfloat16, device="cuda")
+    dec_scale = 1.0 / math.sqrt(192.0)
+    for _ in range(3):
+        hs.hisparse_sparse_mla_decode(g["pool"], stream, w.B, DECODE_HEADS, w.k, 0, q, g["out"],
+                                      dec_scale, out)
+    dec_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+    torch.cuda.synchronize()
+    for e in dec_ev:
+        e[0].record(stream)
+        hs.hisparse_sparse_mla_decode(g["pool"], stream, w.B, DECODE_HEADS, w.k, 0, q, g["out"],
+                                      dec_scale, out)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = float(np.median([e[0].elapsed_time(e[1]) for e in dec_ev]))
+    n_valid = w.valid_entries(last)
+    dec_flop = 2.0 * n_valid * DECODE_HEADS * (576 + 512)
+    dec_bytes = n_valid * ROW_BYTES + w.B * DECODE_HEADS * (576 + 512) * 2 + w.B * w.k * 4
+    dec_tflops = dec_flop / (dec_ms * 1e-3) / 1e12
+    assert torch.isfinite(out.float()).all()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -335,6 +409,20 @@ def main():
             "cold_step0_plan_ms": float(np.median([c[0] for c in cold])) if cold else None,
         },
         "cpu_baseline": cpu,
+        "consumer_sparse_mla_decode": {
+            "kernel": "sparse_mla_decode (128 heads, fp8 latent + bf16 rope rows, bf16 MFMA)",
+            "ms_per_call": dec_ms,
+            "bound": "mfma",
+            "achieved": dec_tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": dec_tflops / MFMA_BF16_PEAK_TFLOPS,
+            "hbm_gbs": dec_bytes / (dec_ms * 1e-3) / 1e9,
+            "hbm_frac": dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "flop_per_call": dec_flop,
+            "algorithmic_bytes_per_call": dec_bytes,
+            "full_step_ms": total_ms / args.steps + dec_ms,
+        },
     }
     print(json.dumps(res), flush=True)
     hs.hisparse_destroy_pool(g["pool"])

@@ -56,48 +56,63 @@ __device__ inline uint4 dequant8(uint32_t w0, uint32_t w1, float sc) {
                     pack_bf16x2(c.x * sc, c.y * sc), pack_bf16x2(d.x * sc, d.y * sc));
 }
 
-// One producer thread's share of one block: a quarter of one row (128 latent
-// bytes with their scale, and 32 rope bytes).
+// One producer thread's share of one block of one row: the four threads of a
+// row take its 16-byte chunks in turn (thread `part` takes latent chunks
+// 4e+part, e = 0..7, and rope chunks part and part+4), so at every step the
+// four threads touch neighbouring 16-byte chunks -- coalesced loads and
+// bank-spread LDS stores.  Chunk 4e+part lies in scale block e/2.
 struct RawPart {
   uint4 lat[8];
   uint4 rope[2];
-  float scale;
+  float4 scale;
   bool valid;
 };
 
-__device__ inline void load_part(RawPart& R, const DecodeParams& p, const int32_t* locb, int key,
+// Location of this thread's key in block `blk` (clamped, always in range).
+__device__ inline int loc_of(const DecodeParams& p, const int32_t* locb, int blk, int key) {
+  const int kk = blk * kKB + key;
+  return locb[kk < p.k ? kk : p.k - 1];
+}
+
+// Issue the loads of one row share; `loc` was fetched two blocks earlier, so
+// no load here waits on another.  Keys past k and invalid locations read
+// row 0 and are stored as zeros.
+__device__ inline void load_part(RawPart& R, const DecodeParams& p, int blk, int key, int loc,
                                  int part) {
-  int64_t loc = -1;
-  if (key < p.k) loc = locb[key];
-  R.valid = loc >= 0 && loc < p.pool_rows;
-  const unsigned char* row = p.pool + (R.valid ? loc : 0) * (int64_t)p.row_bytes;
-  const uint4* lat = (const uint4*)(row + 128 * part);
+  R.valid = (blk * kKB + key < p.k) && loc >= 0 && (int64_t)loc < p.pool_rows;
+  const unsigned char* row = p.pool + (int64_t)(R.valid ? loc : 0) * p.row_bytes;
+  const uint4* chunks = (const uint4*)row;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) R.lat[e] = lat[e];
-  R.scale = *(const float*)(row + kLat + 4 * part);
-  const uint4* rope = (const uint4*)(row + kLat + 16 + 32 * part);
-  R.rope[0] = rope[0];
-  R.rope[1] = rope[1];
+  for (int e = 0; e < 8; ++e) R.lat[e] = chunks[4 * e + part];
+  R.scale = *(const float4*)(row + kLat);
+  const uint4* rope = (const uint4*)(row + kLat + 16);
+  R.rope[0] = rope[part];
+  R.rope[1] = rope[part + 4];
 }
 
 __device__ inline void store_part(const RawPart& R, unsigned char* tile, uint8_t* vflag, int key,
                                   int part) {
-  uint4* dst = (uint4*)(tile + key * kRowStrideBytes + 2 * 128 * part);
-  uint4* rdst = (uint4*)(tile + key * kRowStrideBytes + 2 * (kLat + 16 * part));
+  uint4* row = (uint4*)(tile + key * kRowStrideBytes);  // 16-byte units of bf16
   if (R.valid) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      dst[2 * e] = dequant8(R.lat[e].x, R.lat[e].y, R.scale);
-      dst[2 * e + 1] = dequant8(R.lat[e].z, R.lat[e].w, R.scale);
+      const float sc = (e >> 1) == 0 ? R.scale.x : (e >> 1) == 1 ? R.scale.y
+                     : (e >> 1) == 2 ? R.scale.z : R.scale.w;
+      const int c = 4 * e + part;  // 16 fp8 -> 32 bytes of bf16 at unit 2c
+      row[2 * c] = dequant8(R.lat[e].x, R.lat[e].y, sc);
+      row[2 * c + 1] = dequant8(R.lat[e].z, R.lat[e].w, sc);
     }
-    rdst[0] = R.rope[0];
-    rdst[1] = R.rope[1];
+    row[kLat / 8 + part] = R.rope[0];
+    row[kLat / 8 + part + 4] = R.rope[1];
   } else {  // masked key: zeros, so that 0-weight products stay finite
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dst[e] = z;
-    rdst[0] = z;
-    rdst[1] = z;
+    for (int e = 0; e < 8; ++e) {
+      row[2 * (4 * e + part)] = z;
+      row[2 * (4 * e + part) + 1] = z;
+    }
+    row[kLat / 8 + part] = z;
+    row[kLat / 8 + part + 4] = z;
   }
   if (part == 0) vflag[key] = R.valid ? 1 : 0;
 }
@@ -115,33 +130,46 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_kernel(DecodeParams 
   const int32_t* locb = p.locs + (int64_t)b * p.k;
   uint8_t* vflags = smem + 2 * kTileBytes;
 
+  if (nb == 0) {  // no entries: O = 0
+    if (wave < 2) {
+      const int h = hg * kHeadsPerGroup + wave * kHeadsPerWave + r16;
+      if (h < p.heads) {
+        uint16_t* orow = p.out + ((int64_t)b * p.heads + h) * kLat;
+        for (int t = 0; t < kLat / 16; ++t) *(uint2*)(orow + 16 * t + 4 * g) = make_uint2(0u, 0u);
+      }
+    }
+    return;
+  }
   if (wave >= 2) {
     // ---------------- producers ----------------
     const int pt = tid - 128;
     const int key = pt >> 2, part = pt & 3;
     // R0 holds even blocks, R1 odd blocks (static indexing keeps them in
-    // registers); block x is loaded two iterations before it is stored.
+    // registers).  Block x is loaded two iterations before it is stored and
+    // its location one more iteration before that.
     RawPart R0, R1;
-    if (nb > 0) {
-      load_part(R0, p, locb, key, part);
-      if (nb > 1) load_part(R1, p, locb, kKB + key, part);
-      store_part(R0, smem, vflags, key, part);
-      if (nb > 2) load_part(R0, p, locb, 2 * kKB + key, part);
-    }
+    const int last = nb - 1;
+    int la = loc_of(p, locb, 0, key);
+    int lb = loc_of(p, locb, min(1, last), key);
+    load_part(R0, p, 0, key, la, part);
+    la = loc_of(p, locb, min(2, last), key);
+    load_part(R1, p, 1, key, lb, part);
+    lb = loc_of(p, locb, min(3, last), key);
+    store_part(R0, smem, vflags, key, part);
+    load_part(R0, p, 2, key, la, part);
+    la = loc_of(p, locb, min(4, last), key);
     __syncthreads();
     for (int blk = 0; blk < nb; blk += 2) {
       // iteration blk (even): store block blk+1 (odd, in R1) into buffer 1
-      if (blk + 1 < nb) {
-        store_part(R1, smem + kTileBytes, vflags + 32, key, part);
-        if (blk + 3 < nb) load_part(R1, p, locb, (blk + 3) * kKB + key, part);
-      }
+      if (blk + 1 < nb) store_part(R1, smem + kTileBytes, vflags + 32, key, part);
+      load_part(R1, p, blk + 3, key, lb, part);
+      lb = loc_of(p, locb, min(blk + 5, last), key);
       __syncthreads();
       if (blk + 1 >= nb) break;
       // iteration blk+1 (odd): store block blk+2 (even, in R0) into buffer 0
-      if (blk + 2 < nb) {
-        store_part(R0, smem, vflags, key, part);
-        if (blk + 4 < nb) load_part(R0, p, locb, (blk + 4) * kKB + key, part);
-      }
+      if (blk + 2 < nb) store_part(R0, smem, vflags, key, part);
+      load_part(R0, p, blk + 4, key, la, part);
+      la = loc_of(p, locb, min(blk + 6, last), key);
       __syncthreads();
     }
     return;
