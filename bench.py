@@ -118,6 +118,17 @@ def reset_state(g):
     g["stats"].zero_()
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, host_buf, g, budget_s=15.0):
     """The oracle as it stands, single-threaded, on the same workload from the
     same initial state, for as many steps as fit in about budget_s seconds."""
@@ -130,19 +141,29 @@ def cpu_baseline(w, host_buf, g, budget_s=15.0):
     rows = 0
     t_total = 0.0
     steps = 0
-    for step in range(w.steps):
-        t0 = time.perf_counter()
-        oracle_resolve(ost, page_size=w.P, max_seq_len=w.max_seq_len,
-                       resident_pages=w.resident_pages, req_idx=w.req_idx,
-                       top_k_tokens=w.top_k[step], seq_lens=w.seq_lens[step],
-                       host_cache_locs=w.host_cache_locs, block_table=w.block_table,
-                       host_pools=[host], host_pool_rows=[w.host_pool_rows])
-        t_total += time.perf_counter() - t0
-        rows += w.valid_entries(step)
-        steps += 1
-        if t_total >= budget_s:
-            break
+    # one host core, the one this thread already runs on
+    prev_aff = os.sched_getaffinity(0)
+    core = os.sched_getcpu() if hasattr(os, "sched_getcpu") else min(prev_aff)
+    if core not in prev_aff:
+        core = min(prev_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        for step in range(w.steps):
+            t0 = time.perf_counter()
+            oracle_resolve(ost, page_size=w.P, max_seq_len=w.max_seq_len,
+                           resident_pages=w.resident_pages, req_idx=w.req_idx,
+                           top_k_tokens=w.top_k[step], seq_lens=w.seq_lens[step],
+                           host_cache_locs=w.host_cache_locs, block_table=w.block_table,
+                           host_pools=[host], host_pool_rows=[w.host_pool_rows])
+            t_total += time.perf_counter() - t0
+            rows += w.valid_entries(step)
+            steps += 1
+            if t_total >= budget_s:
+                break
+    finally:
+        os.sched_setaffinity(0, prev_aff)
     return {"value": rows / t_total, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "pinned_core": core, "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count(),
             "sample": "first %d of the %d decode steps of the same workload, all %d batch rows, "
                       "single-threaded C oracle including its row copies (%.2f s, %.1f ms/step)"
                       % (steps, w.steps, w.B, t_total, 1e3 * t_total / steps)}
