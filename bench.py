@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the HiSparse swap-in resolver on one MI355X.
 
-A step is one decode step of the resolver (hisparse_resolve = plan kernel +
-miss-copy kernel) over the DSA-decode workload: 64 long requests with
+A step is one decode step of the resolver (hisparse_resolve: at this batch
+one kernel that plans and copies the misses) over the DSA-decode workload: 64 long requests with
 seq_len U[32768, 131072] plus 8 short fast-path requests, top-k 2048,
 4096 hot slots, 656-byte fp8 sparse-MLA rows, 90 % of each step's top-k kept
 from the previous step, 5 % from the newest 2048 positions, 5 % uniform,
@@ -10,9 +10,9 @@ seq_len + 1 per step.  Inputs (top-k traces, host_cache_locs, state) are in
 HBM and the host pool in pinned host memory before the timed region starts.
 
 Prints one JSON line: rows resolved per second over the timed steps, the
-roofline of the dominant kernel (the miss copy, bound by the host link),
-the roofline of the plan kernel (HBM), and the CPU oracle's rate on a
-bounded sample of the same workload.
+roofline of the dominant kernel (the fused plan + miss copy, bound by the
+host link), the split entry points' plan kernel (HBM) and copy kernel, and
+the CPU oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -39,6 +39,7 @@ ROW_BYTES = 656
 KERNEL_SOURCES = {
     "gather_copy": "hierarchical_sparse_attention_hisparse_amd/csrc/gather.hip",
     "resolve": "hierarchical_sparse_attention_hisparse_amd/csrc/resolve.hip",
+    "resolve_fused": "hierarchical_sparse_attention_hisparse_amd/csrc/resolve.hip",
 }
 
 
@@ -214,21 +215,19 @@ def main():
     g = setup_gpu(w, torch, hs, host_buf)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        """One decode step.  Without events it is the single fused entry
-        point; with events the same two kernels are enqueued through the
-        split entry points with an event between them."""
-        if ev is None:
-            hs.hisparse_resolve(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i], g["seq"][i],
-                                g["locs"], None, g["st"], g["lru"], g["clk"], g["out"], g["stats"])
-            return
-        ev[0].record(stream)
+    def step(i):
+        """One decode step: the single-call entry point.  At this batch it runs
+        one kernel that plans and copies the misses into every layer."""
+        hs.hisparse_resolve(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i], g["seq"][i],
+                            g["locs"], None, g["st"], g["lru"], g["clk"], g["out"], g["stats"])
+
+    def split_plan(i, stats=True):
         hs.hisparse_resolve_plan(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i],
                                  g["seq"][i], g["locs"], None, g["st"], g["lru"], g["clk"],
-                                 g["out"], g["stats"])
-        ev[1].record(stream)
-        hs.hisparse_gather_copy(g["pool"], stream, w.B, 0, w.L, g["stats"])
-        ev[2].record(stream)
+                                 g["out"], g["stats"] if stats else None)
+
+    def restore(snap):
+        g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
 
     log("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
@@ -249,6 +248,12 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     stats_after = g["stats"].cpu().numpy().astype(np.uint64)
     if args.profile_steps:
+        # the same steps through the split entry points (plan-only kernel and
+        # separate copy kernel), then the decode consumer
+        restore(snap)
+        for j in range(args.steps):
+            split_plan(args.warmup + j, stats=False)
+            hs.hisparse_gather_copy(g["pool"], stream, w.B, 0, w.L, None)
         q = make_queries(w.B, DECODE_HEADS, seed=55, device="cuda")
         out = torch.empty((w.B, DECODE_HEADS, 512), dtype=torch.bfloat16, device="cuda")
         for _ in range(5):
@@ -258,41 +263,37 @@ def main():
         log("timed %.3f ms over %d steps" % (total_ms, args.steps))
         return
 
-    # Per-kernel durations, from the same state as the timed region:
+    # The split entry points on the same steps from the same state, for the
+    # per-kernel figures of the plan and the separate copy:
     #  - plan: the K plan launches back to back between two events (the plan
-    #    of step j+1 does not read anything the copy of step j writes);
+    #    of step j+1 reads nothing the copy of step j writes);
     #  - copy: after each step's plan, COPY_REPS back-to-back launches of that
     #    step's copy between two events (re-copying a plan rewrites the same
-    #    bytes), so launch latency is amortised the way it is in the step.
+    #    bytes), so launch latency is amortised the way it is in a step.
     COPY_REPS = 4
-    log("per-kernel timing replay of the %d steps" % args.steps)
-    g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+    log("split-path replay of the %d steps" % args.steps)
+    restore(snap)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for j in range(args.steps):
-        i = args.warmup + j
-        hs.hisparse_resolve_plan(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i],
-                                 g["seq"][i], g["locs"], None, g["st"], g["lru"], g["clk"],
-                                 g["out"], g["stats"])
+        split_plan(args.warmup + j, stats=False)
     e1.record(stream)
     torch.cuda.synchronize()
-    plan_ms = np.array([e0.elapsed_time(e1) / args.steps])
-    g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+    plan_ms = e0.elapsed_time(e1) / args.steps
+    restore(snap)
     cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for j in range(args.steps):
-        i = args.warmup + j
-        hs.hisparse_resolve_plan(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i],
-                                 g["seq"][i], g["locs"], None, g["st"], g["lru"], g["clk"],
-                                 g["out"], g["stats"])
+        split_plan(args.warmup + j, stats=False)
         cev[j][0].record(stream)
         for _ in range(COPY_REPS):
             hs.hisparse_gather_copy(g["pool"], stream, w.B, 0, w.L, None)
         cev[j][1].record(stream)
     torch.cuda.synchronize()
-    copy_ms = np.array([cev[j][0].elapsed_time(cev[j][1]) / COPY_REPS for j in range(args.steps)])
+    copy_ms = float(np.mean([cev[j][0].elapsed_time(cev[j][1]) / COPY_REPS
+                             for j in range(args.steps)]))
 
     d = (stats_after - stats_before).astype(np.int64)
     hits, misses, resident, fast, trips = [int(x) for x in d]
@@ -302,9 +303,10 @@ def main():
                          (w.seq_lens[args.warmup + j][:, None] > w.S)).sum())
                     for j in range(args.steps))
     value = rows / (total_ms * 1e-3)
+    step_ms = total_ms / args.steps
 
     # algorithmic bytes (what the method must move), per launch
-    miss_bytes = misses * ROW_BYTES * w.L / args.steps          # host link, per copy launch
+    miss_bytes = misses * ROW_BYTES * w.L / args.steps          # host link, per step
     n_long = int((w.seq_lens[args.warmup] > w.S).sum())
     n_fast = w.B - n_long
     # long rows read top-k + slot map + stamps and write row IDs; every touched
@@ -313,34 +315,65 @@ def main():
     per_step = lambda x: x / args.steps
     plan_bytes = (n_long * (8 * w.k + 8 * w.S) + per_step(4 * (hits + misses) + 12 * misses)
                   + n_fast * 4 * w.k + per_step(12 * fast) + w.B * 16)
-    copy_gbs = miss_bytes / (copy_ms.mean() * 1e-3) / 1e9
-    plan_gbs = plan_bytes / (plan_ms.mean() * 1e-3) / 1e9
+    step_gbs = miss_bytes / (step_ms * 1e-3) / 1e9
+    copy_gbs = miss_bytes / (copy_ms * 1e-3) / 1e9
+    plan_gbs = plan_bytes / (plan_ms * 1e-3) / 1e9
+    traffic_fused = load_traffic("resolve_fused")
     traffic_copy = load_traffic("gather_copy")
     traffic_plan = load_traffic("resolve")
 
     # side measurements (not in the timed region)
     log("measuring H2D memcpy peak")
     h2d = measure_h2d_peak(torch)
-    cold = []
-    if args.cold_reps > 0:
-        log("cold step 0 x %d from reset state" % args.cold_reps)
-        for _ in range(args.cold_reps):
-            reset_state(g)
-            torch.cuda.synchronize()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(0, ev)
-            torch.cuda.synchronize()
-            m0 = int(g["stats"][1].item())
-            cold.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), m0))
-    cold_copy_ms = float(np.median([c[1] for c in cold])) if cold else None
-    cold_misses = cold[0][2] if cold else 0
-    cold_gbs = cold_misses * ROW_BYTES * w.L / (cold_copy_ms * 1e-3) / 1e9 if cold else None
 
-    # The decode consumer on the rows of the last timed step (config 5 shape:
-    # 128 heads, 576-dim bf16 queries, softmax scale 1/sqrt(192)).
+    def cold_step(reps, locs, topk, seq):
+        """A step from empty hot buffers (every valid entry misses), repeated
+        from reset state; returns (median ms, misses)."""
+        st = torch.full_like(g["st"], -1)
+        lru = torch.zeros_like(g["lru"])
+        clk = torch.zeros_like(g["clk"])
+        stats = torch.zeros(5, dtype=torch.int64, device="cuda")
+        ms = []
+        for _ in range(reps):
+            st.fill_(-1); lru.zero_(); clk.zero_(); stats.zero_()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            hs.hisparse_resolve(g["pool"], stream, w.B, w.k, g["req"], topk, seq, locs, None,
+                                st, lru, clk, g["out"], stats)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ms)), int(stats[1].item())
+
+    cold_ms = cold_misses = cold_gbs = None
+    seq_ms = seq_misses = seq_gbs = None
+    if args.cold_reps > 0:
+        log("cold step 0 x %d from empty hot buffers" % args.cold_reps)
+        cold_ms, cold_misses = cold_step(args.cold_reps, g["locs"], g["topk"][0], g["seq"][0])
+        cold_gbs = cold_misses * ROW_BYTES * w.L / (cold_ms * 1e-3) / 1e9
+        # Zero-copy sequential ceiling through the same kernel: every request
+        # asks for positions 0..k-1 whose host rows are consecutive across the
+        # whole batch, so the misses read one contiguous run of host memory.
+        log("sequential zero-copy ceiling x %d" % args.cold_reps)
+        req_np = w.req_idx.astype(np.int64)
+        locs_seq = torch.zeros((w.R, w.max_seq_len), dtype=torch.int64, device="cuda")
+        ar = torch.arange(w.k, dtype=torch.int64, device="cuda")
+        for b in range(w.B):
+            if req_np[b] >= 0:
+                locs_seq[int(req_np[b]), :w.k] = b * w.k + ar
+        topk_seq = ar.to(torch.int32).repeat(w.B, 1).contiguous()
+        seq_seq = torch.full((w.B,), w.S + 1, dtype=torch.int32, device="cuda")
+        assert w.B * w.k <= w.host_pool_rows
+        seq_ms, seq_misses = cold_step(args.cold_reps, locs_seq, topk_seq, seq_seq)
+        seq_gbs = seq_misses * ROW_BYTES * w.L / (seq_ms * 1e-3) / 1e9
+        del locs_seq
+
+    # The decode consumer on the rows of the last timed step (128 heads,
+    # 576-dim bf16 queries, softmax scale 1/sqrt(192)).
     log("sparse-MLA decode consumer")
     last = args.warmup + args.steps - 1
-    g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+    restore(snap)
     for j in range(args.steps):
         step(args.warmup + j)
     q = make_queries(w.B, DECODE_HEADS, seed=55, device="cuda")
@@ -349,15 +382,16 @@ def main():
     for _ in range(3):
         hs.hisparse_sparse_mla_decode(g["pool"], stream, w.B, DECODE_HEADS, w.k, 0, q, g["out"],
                                       dec_scale, out)
-    dec_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+    DEC_REPS = 20
+    de = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
-    for e in dec_ev:
-        e[0].record(stream)
+    de[0].record(stream)
+    for _ in range(DEC_REPS):
         hs.hisparse_sparse_mla_decode(g["pool"], stream, w.B, DECODE_HEADS, w.k, 0, q, g["out"],
                                       dec_scale, out)
-        e[1].record(stream)
+    de[1].record(stream)
     torch.cuda.synchronize()
-    dec_ms = float(np.median([e[0].elapsed_time(e[1]) for e in dec_ev]))
+    dec_ms = de[0].elapsed_time(de[1]) / DEC_REPS
     n_valid = w.valid_entries(last)
     dec_flop = 2.0 * n_valid * DECODE_HEADS * (576 + 512)
     dec_bytes = n_valid * ROW_BYTES + w.B * DECODE_HEADS * (576 + 512) * 2 + w.B * w.k * 4
@@ -369,6 +403,9 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(w, host_buf, g)
 
+    def traffic_of(t):
+        return (t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]) if t else None
+
     res = {
         "metric": METRIC,
         "value": value,
@@ -376,7 +413,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": total_ms / args.steps,
+        "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -391,30 +428,42 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": "gather_copy (miss rows, pinned host -> HBM)",
+            "kernel": "resolve_kernel<4,2,true>: plan + fused miss copy, one launch per step",
             "bound": "host_link",
-            "achieved": copy_gbs,
+            "achieved": step_gbs,
             "peak": HOST_LINK_PEAK_GBS,
             "unit": "GB/s",
-            "frac": copy_gbs / HOST_LINK_PEAK_GBS,
-            "traffic": (traffic_copy["fetch_bytes_per_launch"] + traffic_copy["write_bytes_per_launch"])
-                       if traffic_copy else None,
+            "frac": step_gbs / HOST_LINK_PEAK_GBS,
+            "traffic": traffic_of(traffic_fused),
             "measured_peak_h2d_memcpy": h2d,
-            "frac_of_measured_peak": copy_gbs / h2d,
+            "frac_of_measured_peak": step_gbs / h2d,
+            "zero_copy_sequential_ceiling": seq_gbs,
+            "frac_of_sequential_ceiling": (step_gbs / seq_gbs) if seq_gbs else None,
             "algorithmic_bytes_per_launch": miss_bytes,
-            "avg_launch_ms": float(copy_ms.mean()),
+            "hbm_algorithmic_bytes_per_launch": plan_bytes + miss_bytes,
+            "avg_launch_ms": step_ms,
         },
         "roofline_plan": {
-            "kernel": "resolve (hit detection, LRU, plan)",
+            "kernel": "resolve_kernel<4,2,false>: plan only (split entry point)",
             "bound": "hbm",
             "achieved": plan_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": plan_gbs / HBM_PEAK_GBS,
-            "traffic": (traffic_plan["fetch_bytes_per_launch"] + traffic_plan["write_bytes_per_launch"])
-                       if traffic_plan else None,
+            "traffic": traffic_of(traffic_plan),
             "algorithmic_bytes_per_launch": plan_bytes,
-            "avg_launch_ms": float(plan_ms.mean()),
+            "avg_launch_ms": plan_ms,
+        },
+        "split_copy": {
+            "kernel": "gather_copy_kernel: separate miss copy (split entry point)",
+            "bound": "host_link",
+            "achieved": copy_gbs,
+            "peak": HOST_LINK_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": copy_gbs / HOST_LINK_PEAK_GBS,
+            "traffic": traffic_of(traffic_copy),
+            "avg_launch_ms": copy_ms,
+            "split_step_ms": plan_ms + copy_ms,
         },
         "detail": {
             "rows_resolved_per_step": rows / args.steps,
@@ -424,10 +473,11 @@ def main():
             "hit_rate_long_rows": hits / max(1, hits + misses),
             "miss_copy_bytes_per_step": miss_bytes,
             "cold_step0_misses": cold_misses,
-            "cold_step0_copy_ms": cold_copy_ms,
+            "cold_step0_ms": cold_ms,
             "cold_step0_copy_gbs": cold_gbs,
-            "cold_step0_frac_of_measured_peak": (cold_gbs / h2d) if cold else None,
-            "cold_step0_plan_ms": float(np.median([c[0] for c in cold])) if cold else None,
+            "cold_step0_frac_of_measured_peak": (cold_gbs / h2d) if cold_gbs else None,
+            "sequential_cold_misses": seq_misses,
+            "sequential_cold_ms": seq_ms,
         },
         "cpu_baseline": cpu,
         "consumer_sparse_mla_decode": {
@@ -442,7 +492,7 @@ def main():
             "hbm_frac": dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "flop_per_call": dec_flop,
             "algorithmic_bytes_per_call": dec_bytes,
-            "full_step_ms": total_ms / args.steps + dec_ms,
+            "full_step_ms": step_ms + dec_ms,
         },
     }
     print(json.dumps(res), flush=True)

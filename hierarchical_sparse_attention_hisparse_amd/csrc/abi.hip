@@ -26,8 +26,11 @@ struct hisparse_pool {
   unsigned char** d_host_ptrs;  // [L] device-mapped host pool pointers
   unsigned char** d_dev_ptrs;   // [L]
   int64_t* d_host_rows;         // [L]
+  uint4* zero_row;              // row_bytes of zeros (source of out-of-range host rows)
   // host copies
   unsigned char** dev_ptrs;     // [L]
+  unsigned char** host_ptrs;    // [L] device-mapped host pool pointers
+  int64_t* host_rows;           // [L]
 };
 
 namespace {
@@ -97,7 +100,8 @@ int check_resolve_args(const hisparse_pool* pool, int32_t batch, int32_t top_k,
 int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t top_k,
                 const int32_t* req_idx, const int32_t* top_k_tokens, const int32_t* seq_lens,
                 const int64_t* host_cache_locs, const int32_t* bt, int32_t* slot_tokens,
-                int32_t* lru_slots, int32_t* lru_clock, int32_t* out, uint64_t* stats) {
+                int32_t* lru_slots, int32_t* lru_clock, int32_t* out, uint64_t* stats,
+                int32_t copy_layers) {
   ResolveParams p;
   p.R = pool->cfg.max_requests;
   p.S = pool->cfg.slots;
@@ -120,6 +124,15 @@ int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   p.plan_dst = pool->plan_dst;
   p.plan_cnt = pool->plan_cnt;
   p.plan_stride = pool->cfg.max_top_k;
+  for (int l = 0; l < kMaxFusedLayers; ++l) {
+    const bool have = l < copy_layers;
+    p.host_pool[l] = have ? pool->host_ptrs[l] : nullptr;
+    p.dev_pool[l] = have ? pool->dev_ptrs[l] : nullptr;
+    p.host_rows[l] = have ? pool->host_rows[l] : 0;
+  }
+  p.zero_row = pool->zero_row;
+  p.units = pool->cfg.row_bytes / 16;
+  p.copy_layers = copy_layers;
   hipError_t e = launch_resolve(p, batch, stream);
   if (e != hipSuccess) return hip_fail(e, "resolve kernel launch");
   return HISPARSE_OK;
@@ -259,14 +272,25 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   pool->device_pool_rows = device_pool_rows;
   pool->max_pages = c.page_size > 0 ? (c.max_seq_len + c.page_size - 1) / c.page_size : 0;
   pool->dev_ptrs = ddev;
+  pool->host_ptrs = hdev;
+  pool->host_rows = (int64_t*)malloc((size_t)L * sizeof(int64_t));
+  if (!pool->host_rows) {
+    free(hdev);
+    free(ddev);
+    free(pool);
+    return fail(HISPARSE_ENOMEM, "host allocation failed");
+  }
+  memcpy(pool->host_rows, host_pool_rows, (size_t)L * sizeof(int64_t));
 
   const size_t entries = (size_t)c.max_batch * c.max_top_k;
   const size_t bytes_src = entries * 8, bytes_dst = entries * 4, bytes_cnt = (size_t)c.max_batch * 4;
   const size_t bytes_tab = (size_t)L * 8;
   unsigned char* ws = nullptr;
-  const size_t total = align16(bytes_src) + align16(bytes_dst) + align16(bytes_cnt) + 3 * align16(bytes_tab);
+  const size_t total = align16(bytes_src) + align16(bytes_dst) + align16(bytes_cnt) +
+                       3 * align16(bytes_tab) + align16((size_t)c.row_bytes);
   e = hipMalloc((void**)&ws, total);
   if (e != hipSuccess) {
+    free(pool->host_rows);
     free(hdev);
     free(ddev);
     free(pool);
@@ -279,16 +303,18 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   pool->plan_cnt = (int32_t*)(ws + o);        o += align16(bytes_cnt);
   pool->d_host_ptrs = (unsigned char**)(ws + o); o += align16(bytes_tab);
   pool->d_dev_ptrs = (unsigned char**)(ws + o);  o += align16(bytes_tab);
-  pool->d_host_rows = (int64_t*)(ws + o);
+  pool->d_host_rows = (int64_t*)(ws + o);  o += align16(bytes_tab);
+  pool->zero_row = (uint4*)(ws + o);
   e = hipMemset(ws, 0, total);
   if (e == hipSuccess) e = hipMemcpy(pool->d_host_ptrs, hdev, bytes_tab, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(pool->d_dev_ptrs, ddev, bytes_tab, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(pool->d_host_rows, host_pool_rows, bytes_tab, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = prepare_resolve(kLdsBudget);
   if (e == hipSuccess) e = prepare_sparse_mla_decode();
-  free(hdev);
   if (e != hipSuccess) {
     (void)hipFree(ws);
+    free(pool->host_rows);
+    free(hdev);
     free(ddev);
     free(pool);
     return hip_fail(e, "pool set-up");
@@ -301,6 +327,8 @@ void hisparse_destroy_pool(hisparse_pool* pool) {
   if (!pool) return;
   if (pool->plan_src) (void)hipFree(pool->plan_src);
   free(pool->dev_ptrs);
+  free(pool->host_ptrs);
+  free(pool->host_rows);
   free(pool);
 }
 
@@ -318,7 +346,7 @@ int hisparse_resolve_plan(hisparse_pool* pool, void* stream, int32_t batch, int3
   if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
   rc = launch_plan(pool, (hipStream_t)stream, batch, top_k, req_idx, top_k_tokens, seq_lens,
                    host_cache_locs, resident_block_table, slot_tokens, lru_slots, lru_clock,
-                   device_buffer_locs, stats);
+                   device_buffer_locs, stats, 0);
   return rc == HISPARSE_OK ? ok() : rc;
 }
 
@@ -349,10 +377,15 @@ int hisparse_resolve(hisparse_pool* pool, void* stream, int32_t batch, int32_t t
   if (rc != HISPARSE_OK) return rc;
   if (batch == 0) return ok();
   if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
+  // Large batches copy inside the plan kernel (each request's workgroup
+  // copies its own misses, so the copy starts as soon as a plan is ready and
+  // there is no second launch); small batches keep the separate copy kernel,
+  // whose many wavefronts keep enough rows in flight on the host link.
+  const bool fuse = batch >= kFuseMinBatch && pool->cfg.num_layers <= kMaxFusedLayers;
   rc = launch_plan(pool, (hipStream_t)stream, batch, top_k, req_idx, top_k_tokens, seq_lens,
                    host_cache_locs, resident_block_table, slot_tokens, lru_slots, lru_clock,
-                   device_buffer_locs, stats);
-  if (rc != HISPARSE_OK) return rc;
+                   device_buffer_locs, stats, fuse ? pool->cfg.num_layers : 0);
+  if (rc != HISPARSE_OK || fuse) return rc == HISPARSE_OK ? ok() : rc;
   rc = launch_copy(pool, (hipStream_t)stream, batch, 0, pool->cfg.num_layers, stats);
   return rc == HISPARSE_OK ? ok() : rc;
 }

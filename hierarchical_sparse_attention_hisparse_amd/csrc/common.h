@@ -28,6 +28,14 @@ constexpr int kVictimRounds = 4;                      // min-extraction rounds b
 // Copy kernel shape.
 constexpr int kCopyThreads = 256;
 
+// Smallest batch whose miss copy runs inside the plan kernel.
+#ifndef HISPARSE_FUSE_MIN_BATCH
+#define HISPARSE_FUSE_MIN_BATCH 8
+#endif
+constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
+constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
+constexpr int kCopyRowsInFlight = 4;  // rows per wavefront per iteration of the fused copy
+
 __host__ __device__ inline int next_pow2(int v) {
   int p = 1;
   while (p < v) p <<= 1;

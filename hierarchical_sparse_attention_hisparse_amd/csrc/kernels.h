@@ -26,6 +26,15 @@ struct ResolveParams {
   int32_t* plan_cnt;
   int32_t plan_stride;
   ResolveLds lds;  // LDS carve-up for (S, k), filled in by launch_resolve
+  // Fused miss copy (copy_layers > 0): after planning, the workgroup copies
+  // its own misses into layers [0, copy_layers) itself.  The per-layer
+  // pointers travel in the kernel arguments (constant, scalar-loaded).
+  const unsigned char* host_pool[kMaxFusedLayers];  // device-mapped host pointers
+  unsigned char* dev_pool[kMaxFusedLayers];
+  int64_t host_rows[kMaxFusedLayers];
+  const uint4* zero_row;                   // device, `units` zero 16-byte units
+  int32_t units;                           // row_bytes / 16
+  int32_t copy_layers;                     // 0 = plan only, else <= kMaxFusedLayers
 };
 
 struct CopyParams {

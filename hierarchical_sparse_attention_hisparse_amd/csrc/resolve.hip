@@ -18,7 +18,10 @@
 //      order; if a few rounds do not cover every miss, a bitonic LDS sort of
 //      the remaining candidates finishes the ranking;
 //   5. the j-th miss takes the j-th victim: token, stamp, row ID and one
-//      (host row, device row) entry of the compact miss plan.
+//      (host row, device row) entry of the compact miss plan;
+//   6. (COPY instances) the workgroup copies its own misses from the pinned
+//      host pools into every layer, one wavefront per row, so each request's
+//      copy starts as soon as its plan exists and no second launch is needed.
 // Resolution order and phases: "vLLM HiSparse 本地 KV 卸载架构" (hot-row lookup
 // and LRU) and "vLLM Hybrid HiSparse 源码实现分析" section 7.2; fast path
 // (seq_len <= S: slot == position, nothing moves): the per-step flow of the
@@ -38,6 +41,9 @@ namespace hisparse {
 namespace {
 
 constexpr uint64_t kEmptyCell = ~0ull;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memory
 
 __device__ inline int lane_prefix(uint64_t m) {  // popcount of m below this lane
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -102,7 +108,8 @@ enum : int {
 };
 static_assert(kScrInts == kResolveScratchInts, "scratch layout");
 
-template <int SPT, int KPT>
+// COPY: the workgroup also copies its misses into p.copy_layers layers.
+template <int SPT, int KPT, bool COPY>
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -380,10 +387,13 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   }
   __syncthreads();
 
-  // Step 5: the j-th miss takes the j-th victim; emit the compact plan.
+  // Step 5: the j-th miss takes the j-th victim; emit the compact plan.  The
+  // fused copy keeps its own copy of the plan in the (now dead) table region.
   int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
   int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
   const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
+  int64_t* f_src = (int64_t*)(smem + L.off_hash);          // [k]
+  int32_t* f_dst = (int32_t*)(smem + L.off_hash + 8 * (size_t)k);  // [k]
   for (int j = tid; j < m_total; j += kResolveThreads) {
     const int i = m_entry[j];
     const int s = victim[j];
@@ -392,8 +402,54 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     lru[s] = c;
     const int row = rowbase + s;
     outb[i] = row;
-    psrc[j] = locr[t];
+    const int64_t h = locr[t];
+    psrc[j] = h;
     pdst[j] = row;
+    if (COPY) {
+      f_src[j] = h;
+      f_dst[j] = row;
+    }
+  }
+
+  // Fused miss copy: one wavefront per (layer, miss) row, lane l carrying
+  // 16-byte unit l, kCopyRowsInFlight rows in flight per wavefront.  Row
+  // indices are wave-uniform (scalar), and the per-layer pointers come from
+  // the kernel arguments.  A host row out of range reads the zero row instead
+  // and counts one tripwire, as the separate copy kernel does.  Past the end
+  // of the list a wavefront repeats its first row of the batch (the same
+  // bytes again), so every load is unconditional.
+  int copy_trips = 0;
+  if (COPY && m_total > 0) {
+    __syncthreads();
+    constexpr int RIF = kCopyRowsInFlight;
+    const int U = p.units;
+    const int total = m_total * p.copy_layers;
+    const int wu = __builtin_amdgcn_readfirstlane(wid);
+#pragma unroll 1
+    for (int u = wu; u < total; u += RIF * kResolveWaves) {
+      const gu4* src[RIF];
+      gu4* dst[RIF];
+#pragma unroll
+      for (int q = 0; q < RIF; ++q) {
+        const bool real = u + q * kResolveWaves < total;
+        const int uq = real ? u + q * kResolveWaves : u;
+        const int l = uq / m_total, j = uq - l * m_total;
+        const int64_t h = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)f_src[j]) |
+                          ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(f_src[j] >> 32)) << 32);
+        const int d = __builtin_amdgcn_readfirstlane(f_dst[j]);
+        const bool ok = h >= 0 && h < p.host_rows[l];
+        src[q] = ok ? (const gu4*)p.host_pool[l] + h * U : (const gu4*)p.zero_row;
+        dst[q] = (gu4*)p.dev_pool[l] + (int64_t)d * U;
+        copy_trips += (real && !ok) ? 1 : 0;
+      }
+      for (int part = lane; part < U; part += kWave) {
+        u32x4 v[RIF];
+#pragma unroll
+        for (int q = 0; q < RIF; ++q) v[q] = src[q][part];
+#pragma unroll
+        for (int q = 0; q < RIF; ++q) dst[q][part] = v[q];
+      }
+    }
   }
 
   if (tid == 0) {
@@ -412,12 +468,17 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       if (tr2) atomicAdd(&p.stats[4], (unsigned long long)tr2);
     }
   }
+  if (copy_trips && lane == 0 && p.stats) atomicAdd(&p.stats[4], (unsigned long long)copy_trips);
 }
 
 template <int SPT, int KPT>
 hipError_t launch_t(const ResolveParams& p, int batch, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((resolve_kernel<SPT, KPT>), dim3(batch), dim3(kResolveThreads), lds, stream,
-                     p);
+  if (p.copy_layers > 0)
+    hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true>), dim3(batch), dim3(kResolveThreads), lds,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false>), dim3(batch), dim3(kResolveThreads), lds,
+                       stream, p);
   return hipGetLastError();
 }
 
@@ -433,7 +494,10 @@ hipError_t launch_k(const ResolveParams& p, int batch, size_t lds, hipStream_t s
 
 template <int SPT, int KPT>
 hipError_t set_attr() {
-  return hipFuncSetAttribute((const void*)resolve_kernel<SPT, KPT>,
+  hipError_t e = hipFuncSetAttribute((const void*)resolve_kernel<SPT, KPT, false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)resolve_kernel<SPT, KPT, true>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
 }
 

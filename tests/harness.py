@@ -31,7 +31,12 @@ def make_host_pools(w, kind="uniform", seed_base=100, gen_device="cuda"):
 class Pair:
     """The GPU side and the oracle side of one workload."""
 
-    def __init__(self, w, host_bufs, with_oracle=True, max_batch=None):
+    def __init__(self, w, host_bufs, with_oracle=True, max_batch=None, mode="resolve"):
+        """mode "resolve": the single-call entry point (which copies inside the
+        plan kernel at batch >= 8 with <= 8 layers); "split": the plan entry
+        point followed by the separate copy entry point."""
+        assert mode in ("resolve", "split")
+        self.mode = mode
         self.w = w
         self.host_bufs = host_bufs
         self.host_np = [h.numpy((w.host_pool_rows, w.row_bytes)) for h in host_bufs]
@@ -79,9 +84,13 @@ class Pair:
         w = self.w
         dst, src = decode_writes(w, step)
         self._copy_rows(dst, src)
-        hs.hisparse_resolve(self.pool, stream, w.B, w.k, self.req_idx, self.topk[step],
-                            self.seq[step], self.locs, self.bt, self.st, self.lru, self.clk,
-                            self.out, self.stats)
+        args = (self.pool, stream, w.B, w.k, self.req_idx, self.topk[step], self.seq[step],
+                self.locs, self.bt, self.st, self.lru, self.clk, self.out, self.stats)
+        if self.mode == "resolve":
+            hs.hisparse_resolve(*args)
+        else:
+            hs.hisparse_resolve_plan(*args)
+            hs.hisparse_gather_copy(self.pool, stream, w.B, 0, w.L, self.stats)
         return dst, src
 
     def oracle_step(self, step, dst, src):
@@ -133,11 +142,12 @@ def _first_diff(name, g, o):
     return "%s differs at %d places, first at %s: gpu=%s oracle=%s" % (name, len(bad), i, g[i], o[i])
 
 
-def run_parity(w, steps=None, kind="uniform", check_rows=True, host_bufs=None, log=None):
+def run_parity(w, steps=None, kind="uniform", check_rows=True, host_bufs=None, log=None,
+               mode="resolve"):
     """Run `steps` steps of workload w on both sides, comparing every step."""
     steps = w.steps if steps is None else steps
     bufs = host_bufs or make_host_pools(w, kind)
-    pair = Pair(w, bufs)
+    pair = Pair(w, bufs, mode=mode)
     try:
         for step in range(steps):
             dst, src = pair.gpu_step(step)

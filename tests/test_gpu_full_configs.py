@@ -38,6 +38,15 @@ def test_config2_dsa_decode_all_steps():
 
 
 @pytest.mark.timeout(600)
+def test_config2_dsa_decode_split_entry_points():
+    """The same workload through the plan and copy entry points (16 steps)."""
+    print("[config2 split] generating 72 rows x 16 steps", flush=True)
+    w = config2_dsa_decode(steps=16)
+    stats = run_parity(w, log=_log("config2 split", every=4), mode="split")
+    assert int(stats[1]) > 0 and int(stats[4]) == 0
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("f", [0.5, 0.9, 0.99])
 def test_config3_mixed_residency(f):
     print("[config3 f=%g] generating 128 x 131072" % f, flush=True)

@@ -30,36 +30,56 @@ def test_config1_tiny_all_steps():
     assert stats[1] > 0 and stats[0] > 0
 
 
-def test_ragged_shapes_fast_path_transition_and_padding():
+# Batches of 8 or more take the copy inside the plan kernel through
+# hisparse_resolve; "split" runs the same steps through the plan and copy
+# entry points.
+MODES = ["resolve", "split"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_ragged_shapes_fast_path_transition_and_padding(mode):
     """S and k not multiples of the wavefront or block size, padding rows,
     fast-path rows that cross seq_len == S during the run, rows with
     seq_len <= k (padded top-k)."""
-    print("[ragged] S=200 k=77 steps=8", flush=True)
+    print("[ragged %s] S=200 k=77 steps=8" % mode, flush=True)
     w = synth("ragged", 21, R=7, S=200, k=77, steps=8,
               n0=[1000, 300, 198, 200, 5000, 60], grow=1, keep=50, recent=10,
               recent_window=100, padding_rows=2)
-    run_parity(w, log=_log("ragged"))
+    run_parity(w, log=_log("ragged"), mode=mode)
 
 
-def test_multi_layer_shared_plan():
-    print("[layers] L=3", flush=True)
-    w = synth("layers", 22, R=4, S=256, k=128, steps=6, n0=[4000, 3000, 2500, 9000], L=3,
+@pytest.mark.parametrize("mode", MODES)
+def test_multi_layer_shared_plan(mode):
+    print("[layers %s] L=3" % mode, flush=True)
+    w = synth("layers", 22, R=10, S=256, k=128, steps=6,
+              n0=[4000, 3000, 2500, 9000, 700, 1200, 5000, 3300, 260], L=3,
               keep=100, recent=8, recent_window=64)
-    run_parity(w, log=_log("layers"))
+    run_parity(w, log=_log("layers"), mode=mode)
 
 
-def test_resident_pages_small():
-    print("[resident] P=16 tail=64", flush=True)
-    w = synth("resident", 23, R=6, S=256, k=128, steps=6, n0=[2048] * 6, keep=90,
+def test_more_layers_than_the_fused_copy_takes():
+    """Nine layers: hisparse_resolve falls back to the separate copy kernel."""
+    print("[layers] L=9", flush=True)
+    w = synth("layers9", 28, R=8, S=128, k=64, steps=3, n0=[900, 700, 500, 2000, 300, 150, 1000, 640],
+              L=9, keep=40)
+    run_parity(w, log=_log("layers9"))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_resident_pages_small(mode):
+    print("[resident %s] P=16 tail=256" % mode, flush=True)
+    w = synth("resident", 23, R=8, S=256, k=128, steps=6, n0=[2048] * 8, keep=90,
               P=16, resident_tail=256)
-    stats = run_parity(w, log=_log("resident"))
+    stats = run_parity(w, log=_log("resident"), mode=mode)
     assert stats[2] > 0
 
 
-def test_top_k_equals_slots():
-    print("[k=S] S=k=2048", flush=True)
-    w = synth("kS", 24, R=3, S=2048, k=2048, steps=4, n0=[50000, 40000, 30000], keep=1800)
-    run_parity(w, log=_log("k=S"))
+@pytest.mark.parametrize("mode", MODES)
+def test_top_k_equals_slots(mode):
+    print("[k=S %s] S=k=2048" % mode, flush=True)
+    w = synth("kS", 24, R=8, S=2048, k=2048, steps=4,
+              n0=[50000, 40000, 30000, 9000, 2100, 2048, 70000, 12345], keep=1800)
+    run_parity(w, log=_log("k=S"), mode=mode)
 
 
 def test_zero_top_k_and_empty_batch():
@@ -81,17 +101,20 @@ def test_zero_top_k_and_empty_batch():
         pair.close()
 
 
-def test_corrupt_state_and_tripwires():
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("layers", [1, 2])
+def test_corrupt_state_and_tripwires(mode, layers):
     """Corrupt slot map (markers below -1, one position in two slots, tokens
     past seq_len), scrambled stamps (forces the full-sort victim path),
     out-of-range host rows and block-table ids, a request index past R."""
-    print("[corrupt]", flush=True)
-    w = synth("corrupt", 26, R=5, S=96, k=40, steps=5, n0=[3000, 2000, 1500, 800],
+    print("[corrupt %s L=%d]" % (mode, layers), flush=True)
+    w = synth("corrupt", 26, R=9, S=96, k=40, steps=5,
+              n0=[3000, 2000, 1500, 800, 4000, 90, 2500, 1200], L=layers,
               keep=30, P=8, resident_tail=64, padding_rows=1)
     rng = np.random.default_rng(5)
     w.req_idx[w.req_idx < 0] = w.R + 2
     bufs = make_host_pools(w)
-    pair = Pair(w, bufs)      # admission uses the clean tables
+    pair = Pair(w, bufs, mode=mode)      # admission uses the clean tables
     try:
         locs = w.host_cache_locs
         locs[rng.random(locs.shape) < 0.05] = -7
