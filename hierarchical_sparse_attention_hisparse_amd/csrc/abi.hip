@@ -27,6 +27,8 @@ struct hisparse_pool {
   unsigned char** d_dev_ptrs;   // [L]
   int64_t* d_host_rows;         // [L]
   uint4* zero_row;              // row_bytes of zeros (source of out-of-range host rows)
+  void* dec_ws;                 // decode split partials, grown on demand
+  size_t dec_ws_bytes;
   // host copies
   unsigned char** dev_ptrs;     // [L]
   unsigned char** host_ptrs;    // [L] device-mapped host pool pointers
@@ -326,6 +328,7 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
 void hisparse_destroy_pool(hisparse_pool* pool) {
   if (!pool) return;
   if (pool->plan_src) (void)hipFree(pool->plan_src);
+  if (pool->dec_ws) (void)hipFree(pool->dec_ws);
   free(pool->dev_ptrs);
   free(pool->host_ptrs);
   free(pool->host_rows);
@@ -412,7 +415,29 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch,
     return fail(HISPARSE_EINVAL, "q_bf16 must be 16-byte, out_bf16 8-byte and locs 4-byte aligned");
   int rc = check_device(pool);
   if (rc != HISPARSE_OK) return rc;
+  const int splits = decode_splits(batch, heads, top_k);
+  const size_t need = decode_workspace_bytes(batch, heads, splits);
+  if (need > pool->dec_ws_bytes) {  // grow the split workspace (synchronises the device)
+    if (pool->dec_ws) {
+      hipError_t fe = hipFree(pool->dec_ws);
+      pool->dec_ws = nullptr;
+      pool->dec_ws_bytes = 0;
+      if (fe != hipSuccess) return hip_fail(fe, "hipFree of the decode workspace");
+    }
+    void* w = nullptr;
+    hipError_t me = hipMalloc(&w, need);
+    if (me != hipSuccess || !w) {
+      (void)hipGetLastError();
+      return fail(HISPARSE_ENOMEM, "hipMalloc(%zu) for the decode workspace: %s", need,
+                  hipGetErrorString(me));
+    }
+    pool->dec_ws = w;
+    pool->dec_ws_bytes = need;
+  }
   DecodeParams d;
+  d.splits = splits;
+  d.part_o = (float*)pool->dec_ws;
+  d.part_ml = d.part_o + need / ((512 + 2) * sizeof(float)) * 512;
   d.pool = pool->dev_ptrs[layer];
   d.pool_rows = pool->device_pool_rows;
   d.row_bytes = pool->cfg.row_bytes;

@@ -36,6 +36,9 @@ constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
 constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
 constexpr int kCopyRowsInFlight = 4;  // rows per wavefront per iteration of the fused copy
 
+// Decode: at most this many key splits per (batch row, head group).
+constexpr int kMaxDecodeSplits = 16;
+
 __host__ __device__ inline int next_pow2(int v) {
   int p = 1;
   while (p < v) p <<= 1;

@@ -62,6 +62,9 @@ struct DecodeParams {
   const uint16_t* q;     // bf16 bits [batch][heads][576]
   const int32_t* locs;   // [batch][k]
   uint16_t* out;         // bf16 bits [batch][heads][512]
+  int32_t splits;        // key splits per (batch row, 128-head group)
+  float* part_o;         // [batch][groups][splits][128][512] unnormalised O
+  float* part_ml;        // [batch][groups][splits][128][2] reference (log2), denominator
 };
 
 hipError_t prepare_resolve(size_t lds_bytes);
@@ -70,5 +73,7 @@ hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStr
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
 hipError_t prepare_sparse_mla_decode();
 size_t decode_lds_bytes();
+int decode_splits(int batch, int heads, int k);
+size_t decode_workspace_bytes(int batch, int heads, int splits);
 
 }  // namespace hisparse

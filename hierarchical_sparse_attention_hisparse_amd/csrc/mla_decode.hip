@@ -8,18 +8,31 @@
 // ("vLLM HiSparse 本地 KV 卸载架构": the attention backend reads the device
 // cache through physical row IDs).
 //
-// One workgroup of 4 wavefronts per (batch row, group of 32 heads):
-//  - waves 2,3 (producers) load 32 rows per block two blocks ahead into
-//    registers, dequantise the latent (fp8 -> f32, times the scale, RNE to
-//    bf16) and write a bf16 tile [32 keys][576 (+8 pad) dims] to LDS;
-//    double-buffered, one barrier per block;
-//  - waves 0,1 (consumers) own 16 heads each: S^T = K Q^T on
-//    v_mfma_f32_16x16x32_bf16 with Q in registers, an online softmax, and
-//    O^T += V^T P^T where P^T comes straight from the S^T accumulator layout
-//    and V^T fragments are read from the same row-major tile with the LDS
-//    transpose load (ds_read_b64_tr_b16).
-// Workgroups are numbered so that the head groups of one batch row land on
-// the same XCD and share its L2.
+// One workgroup of 4 wavefronts per (batch row, group of 128 heads, split of
+// the keys).  All four wavefronts share the loading: each block of 32 keys is
+// fetched a block ahead into registers, then dequantised (fp8 -> f32, times
+// the scale, RNE to bf16) and written to a double-buffered bf16 tile
+// [32 keys][576 (+8 pad) dims] in LDS between the MFMAs of the previous
+// block's score loop; one barrier per block.  Each wavefront
+// computes the scores of its own 32 heads, so every K fragment read from LDS
+// feeds two MFMAs (LDS instruction issue, not bytes, bounds this loop on
+// gfx950), and then O for a quarter of the dims of all 128 heads, so every
+// transposed V fragment is read once per workgroup and feeds eight MFMAs:
+//  - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q held in registers;
+//  - a softmax against a fixed reference per head: the maximum of the first
+//    block holding a valid key for that head.  P = 2^(x - ref) is exact in
+//    fp32 and bf16 for any x up to ref + 64 (log2 units), so O is never
+//    rescaled in the loop (a conditional rescale of the accumulator registers
+//    forces the compiler to spill them).  If some score exceeds its reference
+//    by more than that, the workgroup runs a second pass over its keys with a
+//    reference that the first pass has shown to be high enough;
+//  - P^T fragments taken straight from the S^T accumulator layout (keys
+//    permuted consistently) are exchanged through LDS (one more barrier);
+//  - O^T += V^T P^T with the V^T fragments read from the same row-major tile
+//    with the LDS transpose load (ds_read_b64_tr_b16).
+// Each workgroup writes its unnormalised O with its reference and
+// denominator, and a second kernel combines the splits of a row and
+// normalises (the same algebra as one pass, in fp32).
 #include "common.h"
 #include "kernels.h"
 
@@ -32,8 +45,21 @@ constexpr int kLat = 512, kDim = 576;
 constexpr int kTileStride = 584;                  // bf16 per tile row (576 + 8 pad)
 constexpr int kRowStrideBytes = kTileStride * 2;  // 1168: conflict-free b128 / tr16 reads
 constexpr int kTileBytes = kKB * kRowStrideBytes;
-constexpr int kHeadsPerWave = 16;
-constexpr int kHeadsPerGroup = 32;
+constexpr int kDecWaves = 4;
+constexpr int kHeadsPerWave = 32;
+constexpr int kHeadsPerGroup = kDecWaves * kHeadsPerWave;  // 128
+constexpr float kMaxExcessLog2 = 64.f;            // largest score above a head's reference (log2)
+constexpr int kRope = kDim - kLat;                // 64
+constexpr int kQRopeStrideBytes = 144;            // 64 bf16 + 16 pad: conflict-free b128 reads
+constexpr int kLatSteps = kLat / 32;              // 16 k-steps over the latent
+constexpr int kQKAhead = 2;                       // LDS reads this many MFMA steps ahead
+constexpr size_t kOffFlags = 2 * (size_t)kTileBytes;
+constexpr size_t kOffOvf = kOffFlags + 64;        // int: a score exceeded its reference by > 2^64
+constexpr size_t kOffQRope = kOffOvf + 16;        // [128 heads][72 bf16] rope part of Q
+constexpr int kHeadTiles = kHeadsPerGroup / 16;    // 8
+constexpr int kDimTilesPerWave = kLat / 16 / kDecWaves;  // 8: O dims 128w..128w+127
+constexpr size_t kOffP = kOffQRope + (size_t)kHeadsPerGroup * kQRopeStrideBytes;  // P^T fragments
+constexpr size_t kPBytes = (size_t)kHeadTiles * 64 * 16;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -41,9 +67,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {  // round to nearest even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // 8 e4m3 bytes (two words) times the block scale -> 8 bf16.
@@ -56,241 +83,397 @@ __device__ inline uint4 dequant8(uint32_t w0, uint32_t w1, float sc) {
                     pack_bf16x2(c.x * sc, c.y * sc), pack_bf16x2(d.x * sc, d.y * sc));
 }
 
-// One producer thread's share of one block of one row: the four threads of a
-// row take its 16-byte chunks in turn (thread `part` takes latent chunks
-// 4e+part, e = 0..7, and rope chunks part and part+4), so at every step the
-// four threads touch neighbouring 16-byte chunks -- coalesced loads and
-// bank-spread LDS stores.  Chunk 4e+part lies in scale block e/2.
+// One thread's share of one key row: the eight threads of a key take its
+// 16-byte latent chunks part, part+8, part+16, part+24 (chunk part+8e lies in
+// scale block e) and rope chunk `part`, so neighbouring threads touch
+// neighbouring chunks.
 struct RawPart {
-  uint4 lat[8];
-  uint4 rope[2];
+  uint4 lat[4];
+  uint4 rope;
   float4 scale;
   bool valid;
 };
 
-// Location of this thread's key in block `blk` (clamped, always in range).
-__device__ inline int loc_of(const DecodeParams& p, const int32_t* locb, int blk, int key) {
-  const int kk = blk * kKB + key;
+// Workgroup barrier for LDS traffic only: the wave's LDS operations complete,
+// while its global loads (rows of the blocks ahead) stay in flight across it.
+// __syncthreads() would also wait for those loads, one memory latency per
+// barrier.  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Location of top-k entry `kk` of this row, at a clamped (in-range) index.
+__device__ inline int loc_at(const DecodeParams& p, const int32_t* locb, int kk) {
   return locb[kk < p.k ? kk : p.k - 1];
 }
 
-// Issue the loads of one row share; `loc` was fetched two blocks earlier, so
-// no load here waits on another.  Keys past k and invalid locations read
-// row 0 and are stored as zeros.
-__device__ inline void load_part(RawPart& R, const DecodeParams& p, int blk, int key, int loc,
-                                 int part) {
-  R.valid = (blk * kKB + key < p.k) && loc >= 0 && (int64_t)loc < p.pool_rows;
+// Issue the loads of one row share.  Entries past k and invalid locations
+// read row 0 and are stored as zeros.
+__device__ inline void load_part(RawPart& R, const DecodeParams& p, int kk, int loc, int part) {
+  R.valid = kk < p.k && loc >= 0 && (int64_t)loc < p.pool_rows;
   const unsigned char* row = p.pool + (int64_t)(R.valid ? loc : 0) * p.row_bytes;
   const uint4* chunks = (const uint4*)row;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) R.lat[e] = chunks[4 * e + part];
+  for (int e = 0; e < 4; ++e) R.lat[e] = chunks[part + 8 * e];
   R.scale = *(const float4*)(row + kLat);
-  const uint4* rope = (const uint4*)(row + kLat + 16);
-  R.rope[0] = rope[part];
-  R.rope[1] = rope[part + 4];
+  R.rope = ((const uint4*)(row + kLat + 16))[part];
+}
+
+// Dequantise half h (8 values) of latent chunk e of this thread's share and
+// write it (16 bytes of bf16) to the key's tile row; a masked key writes
+// zeros.  Branch-free, so that it can sit between the MFMAs of the score loop.
+__device__ inline void store_half(const RawPart& R, unsigned char* tile, int key, int part, int e,
+                                  int h) {
+  uint4* row = (uint4*)(tile + key * kRowStrideBytes);  // 16-byte units of bf16
+  const float sc = e == 0 ? R.scale.x : e == 1 ? R.scale.y : e == 2 ? R.scale.z : R.scale.w;
+  const uint32_t m = R.valid ? ~0u : 0u;
+  uint4 v = h == 0 ? dequant8(R.lat[e].x, R.lat[e].y, sc) : dequant8(R.lat[e].z, R.lat[e].w, sc);
+  v.x &= m; v.y &= m; v.z &= m; v.w &= m;
+  row[2 * (part + 8 * e) + h] = v;  // 16 fp8 -> 32 bytes of bf16 at unit 2c, c = part + 8e
+}
+
+__device__ inline void store_chunk(const RawPart& R, unsigned char* tile, int key, int part, int e) {
+  store_half(R, tile, key, part, e, 0);
+  store_half(R, tile, key, part, e, 1);
+}
+
+// The rope chunk and the key's validity flag.
+__device__ inline void store_tail(const RawPart& R, unsigned char* tile, uint8_t* vflag, int key,
+                                  int part) {
+  uint4* row = (uint4*)(tile + key * kRowStrideBytes);
+  const uint32_t m = R.valid ? ~0u : 0u;
+  row[kLat / 8 + part] = make_uint4(R.rope.x & m, R.rope.y & m, R.rope.z & m, R.rope.w & m);
+  if (part == 0) vflag[key] = R.valid ? 1 : 0;
 }
 
 __device__ inline void store_part(const RawPart& R, unsigned char* tile, uint8_t* vflag, int key,
                                   int part) {
-  uint4* row = (uint4*)(tile + key * kRowStrideBytes);  // 16-byte units of bf16
-  if (R.valid) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float sc = (e >> 1) == 0 ? R.scale.x : (e >> 1) == 1 ? R.scale.y
-                     : (e >> 1) == 2 ? R.scale.z : R.scale.w;
-      const int c = 4 * e + part;  // 16 fp8 -> 32 bytes of bf16 at unit 2c
-      row[2 * c] = dequant8(R.lat[e].x, R.lat[e].y, sc);
-      row[2 * c + 1] = dequant8(R.lat[e].z, R.lat[e].w, sc);
-    }
-    row[kLat / 8 + part] = R.rope[0];
-    row[kLat / 8 + part + 4] = R.rope[1];
-  } else {  // masked key: zeros, so that 0-weight products stay finite
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      row[2 * (4 * e + part)] = z;
-      row[2 * (4 * e + part) + 1] = z;
-    }
-    row[kLat / 8 + part] = z;
-    row[kLat / 8 + part + 4] = z;
-  }
-  if (part == 0) vflag[key] = R.valid ? 1 : 0;
+  for (int e = 0; e < 4; ++e) store_chunk(R, tile, key, part, e);
+  store_tail(R, tile, vflag, key, part);
 }
 
-__global__ __launch_bounds__(256, 2) void sparse_mla_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  const int x = blockIdx.x;
-  const int b = (x / (8 * HG)) * 8 + (x % 8);
-  const int hg = (x / 8) % HG;
-  if (b >= p.batch) return;
+  const int NS = p.splits;
+  int x = blockIdx.x;
+  const int sp = x % NS;
+  x /= NS;
+  const int hg = x % HG;
+  const int b = x / HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int nb = (p.k + kKB - 1) / kKB;
+  const int per = (nb + NS - 1) / NS;
+  const int blk0 = sp * per;
+  const int nblk = max(0, min(nb, blk0 + per) - blk0);
   const int32_t* locb = p.locs + (int64_t)b * p.k;
-  uint8_t* vflags = smem + 2 * kTileBytes;
+  uint8_t* vflags = smem + kOffFlags;
+  // First head of this wave.  Waves past the last head compute on clamped
+  // queries and their partials are never read: keeping every wave on the same
+  // path keeps the accumulators in registers.
+  const int hw = hg * kHeadsPerGroup + wave * kHeadsPerWave;
+  const int key = tid >> 3, part = tid & 7;                   // loading role
 
-  if (nb == 0) {  // no entries: O = 0
-    if (wave < 2) {
-      const int h = hg * kHeadsPerGroup + wave * kHeadsPerWave + r16;
-      if (h < p.heads) {
-        uint16_t* orow = p.out + ((int64_t)b * p.heads + h) * kLat;
-        for (int t = 0; t < kLat / 16; ++t) *(uint2*)(orow + 16 * t + 4 * g) = make_uint2(0u, 0u);
-      }
-    }
-    return;
-  }
-  if (wave >= 2) {
-    // ---------------- producers ----------------
-    const int pt = tid - 128;
-    const int key = pt >> 2, part = pt & 3;
-    // R0 holds even blocks, R1 odd blocks (static indexing keeps them in
-    // registers).  Block x is loaded two iterations before it is stored and
-    // its location one more iteration before that.
-    RawPart R0, R1;
-    const int last = nb - 1;
-    int la = loc_of(p, locb, 0, key);
-    int lb = loc_of(p, locb, min(1, last), key);
-    load_part(R0, p, 0, key, la, part);
-    la = loc_of(p, locb, min(2, last), key);
-    load_part(R1, p, 1, key, lb, part);
-    lb = loc_of(p, locb, min(3, last), key);
-    store_part(R0, smem, vflags, key, part);
-    load_part(R0, p, 2, key, la, part);
-    la = loc_of(p, locb, min(4, last), key);
-    __syncthreads();
-    for (int blk = 0; blk < nb; blk += 2) {
-      // iteration blk (even): store block blk+1 (odd, in R1) into buffer 1
-      if (blk + 1 < nb) store_part(R1, smem + kTileBytes, vflags + 32, key, part);
-      load_part(R1, p, blk + 3, key, lb, part);
-      lb = loc_of(p, locb, min(blk + 5, last), key);
-      __syncthreads();
-      if (blk + 1 >= nb) break;
-      // iteration blk+1 (odd): store block blk+2 (even, in R0) into buffer 0
-      if (blk + 2 < nb) store_part(R0, smem, vflags, key, part);
-      load_part(R0, p, blk + 4, key, la, part);
-      la = loc_of(p, locb, min(blk + 6, last), key);
-      __syncthreads();
-    }
-    return;
-  }
-
-  // ---------------- consumers ----------------
-  const int h0 = hg * kHeadsPerGroup + wave * kHeadsPerWave;
-  const int h = h0 + r16;
-  const bool head_ok = h < p.heads;
-  bf16x8 qf[kDim / 32];
-  {
-    const bf16x8* qrow = (const bf16x8*)(p.q + ((int64_t)b * p.heads + (head_ok ? h : 0)) * kDim);
+  // The latent part of Q for this wave's two 16-head tiles in the MFMA B
+  // layout (registers); its rope part goes to LDS.
+  bf16x8 qf[2][kLatSteps];
+  unsigned char* qrope = smem + kOffQRope;
 #pragma unroll
-    for (int ks = 0; ks < kDim / 32; ++ks) qf[ks] = qrow[ks * 4 + g];
-  }
-  f32x4 o[kLat / 16];
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = hw + 16 * ht + r16;
+    const bf16x8* qrow = (const bf16x8*)(p.q + ((int64_t)b * p.heads + (h < p.heads ? h : 0)) * kDim);
 #pragma unroll
-  for (int t = 0; t < kLat / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int ks = 0; ks < kLatSteps; ++ks) qf[ht][ks] = qrow[ks * 4 + g];
+  }
+  {  // rope part of Q: 128 heads x 8 chunks of 16 bytes, 4 per thread
+    const int HGh = hg * kHeadsPerGroup;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = tid + 256 * j;       // chunk id
+      const int hl = c >> 3, ch = c & 7;  // local head, 16-byte chunk of its rope
+      const int h = HGh + hl;
+      const uint4* src = (const uint4*)(p.q + ((int64_t)b * p.heads + (h < p.heads ? h : 0)) * kDim + kLat);
+      *(uint4*)(qrope + hl * kQRopeStrideBytes + 16 * ch) = src[ch];
+    }
+  }
+  // O^T accumulators of dims 128*wave..+127 (8 tiles of 16) for all 128 heads
+  // of the group (8 tiles of 16).
+  f32x4 o[kHeadTiles][kDimTilesPerWave];
+  float m_run[2], l_run[2];
+  float m_ref2[2] = {-INFINITY, -INFINITY};
   const float sl2 = p.scale * 1.4426950408889634f;  // scale * log2(e)
-  __syncthreads();
+  int* s_ovf = (int*)(smem + kOffOvf);
 
-  for (int blk = 0; blk < nb; ++blk) {
-    const unsigned char* tile = smem + (blk & 1) * kTileBytes;
-    const uint8_t* vf = vflags + 32 * (blk & 1);
-    // S^T = K Q^T for the block's 32 keys (two 16-key tiles, two chains each).
-    f32x4 s[2][2];
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) s[m][0] = s[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < kHeadTiles; ++ht)
 #pragma unroll
-    for (int ks = 0; ks < kDim / 32; ++ks) {
+      for (int t = 0; t < kDimTilesPerWave; ++t) o[ht][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const bf16x8 a = *(const bf16x8*)(tile + (16 * m + r16) * kRowStrideBytes + 2 * (32 * ks + 8 * g));
-        s[m][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[m][ks & 1], 0, 0, 0);
-      }
+    for (int ht = 0; ht < 2; ++ht) {
+      m_run[ht] = m_ref2[ht];  // -inf in the first pass: set by the first valid block
+      l_run[ht] = 0.f;
     }
-    // Online softmax over this block for head h (column of S^T).
-    float xv[2][4];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const uint32_t vw = *(const uint32_t*)(vf + 16 * m + 4 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sv = s[m][0][i] + s[m][1][i];
-        xv[m][i] = ((vw >> (8 * i)) & 0xFF) ? sv * sl2 : -INFINITY;
-        mloc = fmaxf(mloc, xv[m][i]);
-      }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    float alpha = 1.f;
-    float pv[2][4];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[m][i] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[m][i] = exp2f(xv[m][i] - m_new);
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) psum += pv[m][i];
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int t = 0; t < kLat / 16; ++t) o[t] *= alpha;
-    }
-    // P^T in the B layout: k-slots 0..3 = keys 4g..4g+3, 4..7 = keys 16+4g..16+4g+3.
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = (__bf16)pv[0][i];
-      pb[4 + i] = (__bf16)pv[1][i];
-    }
-    // O^T += V^T P^T: the V^T fragment of dims 16t..16t+15 for the same key
-    // order, read transposed from the row-major tile.
-    const int tk0 = 4 * g + (r16 >> 2);  // key row this lane addresses
-    const int td = 4 * (r16 & 3);        // dim offset inside the 16-dim tile
-#pragma unroll
-    for (int t = 0; t < kLat / 16; ++t) {
-      const unsigned char* a0 = tile + tk0 * kRowStrideBytes + 2 * (16 * t + td);
-      const unsigned char* a1 = a0 + 16 * kRowStrideBytes;
-      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
-      const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[t], 0, 0, 0);
+    float m_hi[2] = {-INFINITY, -INFINITY};
+    int ovf = 0;
+    if (tid == 0) *s_ovf = 0;
+
+    RawPart R;
+    int loc_n = 0;
+    if (nblk > 0) {
+      const int last = nb - 1;
+      load_part(R, p, blk0 * kKB + key, loc_at(p, locb, blk0 * kKB + key), part);
+      const int loc1 = loc_at(p, locb, min(blk0 + 1, last) * kKB + key);
+      loc_n = loc_at(p, locb, min(blk0 + 2, last) * kKB + key);
+      store_part(R, smem, vflags, key, part);
+      load_part(R, p, (blk0 + 1) * kKB + key, loc1, part);
     }
     __syncthreads();
+
+    for (int i = 0; i < nblk; ++i) {
+      const unsigned char* tile = smem + (i & 1) * kTileBytes;
+      const uint8_t* vf = vflags + 32 * (i & 1);
+      // Block i+1 goes into the other buffer, last read before the previous
+      // barrier (past the end of the split it is written and never read).
+      unsigned char* ntile = smem + ((i + 1) & 1) * kTileBytes;
+      uint8_t* nvf = vflags + 32 * ((i + 1) & 1);
+      bf16x8 pb[2];
+      {
+        // S^T = K Q^T: 2 key tiles x 2 head tiles, K fragments shared by both head tiles.
+        f32x4 s[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K fragments (and, for the rope steps, Q fragments) are read
+        // kQKAhead steps ahead of the MFMAs that use them.
+        const unsigned char* ka = tile + r16 * kRowStrideBytes + 16 * g;
+        const unsigned char* qa = qrope + (wave * kHeadsPerWave + r16) * kQRopeStrideBytes + 16 * g;
+        bf16x8 fa0[kQKAhead + 1], fa1[kQKAhead + 1], fb0[kQKAhead + 1], fb1[kQKAhead + 1];
+#pragma unroll
+        for (int ks = 0; ks < kDim / 32 + kQKAhead; ++ks) {
+          if (ks < kDim / 32) {  // issue the reads of step ks
+            const int sl = ks % (kQKAhead + 1);
+            fa0[sl] = *(const bf16x8*)(ka + 64 * ks);
+            fa1[sl] = *(const bf16x8*)(ka + 16 * kRowStrideBytes + 64 * ks);
+            if (ks >= kLatSteps) {
+              fb0[sl] = *(const bf16x8*)(qa + 64 * (ks - kLatSteps));
+              fb1[sl] = *(const bf16x8*)(qa + 16 * kQRopeStrideBytes + 64 * (ks - kLatSteps));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const int c = ks - kQKAhead;  // step whose MFMAs issue now
+          if (c >= 0) {
+            const int sl = c % (kQKAhead + 1);
+            const bf16x8 b0 = c < kLatSteps ? qf[0][c < kLatSteps ? c : 0] : fb0[sl];
+            const bf16x8 b1 = c < kLatSteps ? qf[1][c < kLatSteps ? c : 0] : fb1[sl];
+            s[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0[sl], b0, s[0][0], 0, 0, 0);
+            s[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0[sl], b1, s[0][1], 0, 0, 0);
+            s[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1[sl], b0, s[1][0], 0, 0, 0);
+            s[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1[sl], b1, s[1][1], 0, 0, 0);
+            // The next block's tile, half a chunk every second step, its VALU
+            // work issued between these MFMAs (which run on the matrix core).
+            if (c % 2 == 1 && c / 2 < 8) {
+              store_half(R, ntile, key, part, c / 4, (c / 2) & 1);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then VALU
+              }
+            }
+            if (c == 16) store_tail(R, ntile, nvf, key, part);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // The loads of block i+2 (always in range), now that R is stored.
+        load_part(R, p, (blk0 + i + 2) * kKB + key, loc_n, part);
+        loc_n = loc_at(p, locb, min(blk0 + i + 3, nb - 1) * kKB + key);
+        // Softmax for head hw+16ht+r16 over the lane's 8 keys (4g..4g+3 and
+        // 16+4g..16+4g+3), against the head's reference m_run.
+        const uint32_t vw[2] = {*(const uint32_t*)(vf + 4 * g), *(const uint32_t*)(vf + 16 + 4 * g)};
+        float xv[2][2][4];
+        float lmax[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xv[ht][kt][e] = ((vw[kt] >> (8 * e)) & 0xFF) ? s[kt][ht][e] * sl2 : -INFINITY;
+              lmax[ht] = fmaxf(lmax[ht], xv[ht][kt][e]);
+            }
+        const bool up0 = lmax[0] > m_run[0] + kMaxExcessLog2;
+        const bool up1 = lmax[1] > m_run[1] + kMaxExcessLog2;
+        if (__ballot(up0 || up1)) {  // first valid block of a head, or an overflow
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            float bm = lmax[ht];
+            bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            int nd = (ht == 0 ? up0 : up1) ? 1 : 0;
+            nd |= __shfl_xor(nd, 16, 64);
+            nd |= __shfl_xor(nd, 32, 64);
+            if (nd) {
+              if (m_run[ht] == -INFINITY) {
+                m_run[ht] = bm;  // nothing accumulated yet: no rescale needed
+              } else {
+                ovf = 1;
+                m_hi[ht] = fmaxf(m_hi[ht], bm);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          float pv[2][4];
+          float ps = 0.f;
+          // no valid key seen yet: every x is -inf, and a finite reference
+          // keeps x - ref at -inf (P = 0) instead of NaN
+          const float mref = m_run[ht] == -INFINITY ? 0.f : m_run[ht];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float xx = xv[ht][kt][e];
+              // v_exp_f32 without denormal range reduction: results below
+              // 2^-126 flush to zero, negligible against the reference's 1
+              pv[kt][e] = __builtin_amdgcn_exp2f(fminf(xx - mref, kMaxExcessLog2));
+              ps += pv[kt][e];
+            }
+          l_run[ht] += ps;
+          // P^T in the B layout: k-slots 0..3 = keys 4g..4g+3, 4..7 = keys 16+4g..16+4g+3.
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb[ht][e] = (__bf16)pv[0][e];
+            pb[ht][4 + e] = (__bf16)pv[1][e];
+          }
+        }
+      }
+      {
+        // Publish this wave's P^T fragments (B layout) for the other waves.
+        bf16x8* pbuf = (bf16x8*)(smem + kOffP);
+        pbuf[(2 * wave) * 64 + lane] = pb[0];
+        pbuf[(2 * wave + 1) * 64 + lane] = pb[1];
+      }
+      lds_barrier();  // P of all 128 heads in LDS
+      {
+        // O^T += V^T P^T over this wave's 128 dims and all 128 heads: every
+        // V^T fragment (read transposed from the row-major tile) feeds 8 MFMAs.
+        const bf16x8* pbuf = (const bf16x8*)(smem + kOffP);
+        bf16x8 pf[kHeadTiles];
+#pragma unroll
+        for (int ht = 0; ht < kHeadTiles; ++ht) pf[ht] = pbuf[ht * 64 + lane];
+        const int tk0 = 4 * g + (r16 >> 2);  // key row this lane addresses
+        const int td = 4 * (r16 & 3);        // dim offset inside the 16-dim tile
+        const unsigned char* va0 =
+            tile + tk0 * kRowStrideBytes + 2 * (16 * kDimTilesPerWave * wave + td);
+        bf16x4 fv0[2], fv1[2];
+        fv0[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0));
+        fv1[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * kRowStrideBytes));
+#pragma unroll
+        for (int t = 0; t < kDimTilesPerWave; ++t) {
+          if (t + 1 < kDimTilesPerWave) {  // the next dim tile's fragment
+            fv0[(t + 1) & 1] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 32 * (t + 1)));
+            fv1[(t + 1) & 1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(va0 + 16 * kRowStrideBytes + 32 * (t + 1)));
+          }
+          const bf16x8 va = {fv0[t & 1][0], fv0[t & 1][1], fv0[t & 1][2], fv0[t & 1][3],
+                             fv1[t & 1][0], fv1[t & 1][1], fv1[t & 1][2], fv1[t & 1][3]};
+#pragma unroll
+          for (int ht = 0; ht < kHeadTiles; ++ht)
+            o[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[ht], o[ht][t], 0, 0, 0);
+        }
+      }
+      lds_barrier();  // this block's tile and P are no longer read
+    }
+    if (ovf) *s_ovf = 1;
+    __syncthreads();
+    const bool again = *s_ovf != 0;  // workgroup-uniform
+    if (!again) break;
+    // Second pass: every score is at most max(reference, the largest block
+    // maximum that exceeded it), so that bound keeps P within 2^64.
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) m_ref2[ht] = fmaxf(m_run[ht], m_hi[ht]);
+    __syncthreads();  // everyone has read the flag before it is cleared
   }
 
-  // Normalise by the softmax denominator and store bf16 O[b][h][d].
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (head_ok) {
-    uint16_t* orow = p.out + ((int64_t)b * p.heads + h) * kLat;
+  // Partial result of this split: unnormalised O (this wave's 128 dims of
+  // every head), and the reference (log2 units) and denominator of this
+  // wave's 32 heads.
+  const int64_t e0 = ((int64_t)(b * HG + hg) * NS + sp) * kHeadsPerGroup;
 #pragma unroll
-    for (int t = 0; t < kLat / 16; ++t) {
-      uint2 w;
-      w.x = pack_bf16x2(o[t][0] * inv, o[t][1] * inv);
-      w.y = pack_bf16x2(o[t][2] * inv, o[t][3] * inv);
-      *(uint2*)(orow + 16 * t + 4 * g) = w;
+  for (int ht = 0; ht < kHeadTiles; ++ht) {
+    float* po = p.part_o + (e0 + 16 * ht + r16) * kLat + 16 * kDimTilesPerWave * wave + 4 * g;
+#pragma unroll
+    for (int t = 0; t < kDimTilesPerWave; ++t) *(f32x4*)(po + 16 * t) = o[ht][t];
+  }
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    float l_tot = l_run[ht];
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int64_t e = e0 + wave * kHeadsPerWave + 16 * ht + r16;
+    if (g == 0) {
+      p.part_ml[2 * e] = m_run[ht];
+      p.part_ml[2 * e + 1] = l_tot;
     }
   }
+}
+
+// Combine the splits of every (batch row, head): O = sum_j w_j O_j / sum_j w_j l_j
+// with w_j = 2^(m_j - max m).  One thread per 4 output dims.
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.batch * p.heads * (kLat / 4);
+  if (idx >= total) return;
+  const int q = (int)(idx % (kLat / 4));
+  const int64_t bh = idx / (kLat / 4);
+  const int h = (int)(bh % p.heads);
+  const int b = (int)(bh / p.heads);
+  const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const int hg = h / kHeadsPerGroup, hl = h - hg * kHeadsPerGroup;
+  const int NS = p.splits;
+  const int64_t e0 = ((int64_t)(b * HG + hg) * NS) * kHeadsPerGroup + hl;
+  float M = -INFINITY;
+  for (int j = 0; j < NS; ++j) M = fmaxf(M, p.part_ml[2 * (e0 + (int64_t)j * kHeadsPerGroup)]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int j = 0; j < NS; ++j) {
+      const int64_t e = e0 + (int64_t)j * kHeadsPerGroup;
+      const float m = p.part_ml[2 * e];
+      if (m == -INFINITY) continue;
+      const float w = exp2f(m - M);
+      L += w * p.part_ml[2 * e + 1];
+      acc += w * *(const f32x4*)(p.part_o + e * kLat + 4 * q);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint2 wv;
+  wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(uint2*)(p.out + ((int64_t)b * p.heads + h) * kLat + 4 * q) = wv;
 }
 
 }  // namespace
 
-size_t decode_lds_bytes() { return 2 * (size_t)kTileBytes + 64; }
+size_t decode_lds_bytes() { return kOffP + kPBytes; }
+
+int decode_splits(int batch, int heads, int k) {
+  const int HG = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const int nb = (k + kKB - 1) / kKB;
+  int s = 256 / (batch * HG > 0 ? batch * HG : 1);
+  if (s > kMaxDecodeSplits) s = kMaxDecodeSplits;
+  if (s > nb) s = nb;
+  return s < 1 ? 1 : s;
+}
+
+size_t decode_workspace_bytes(int batch, int heads, int splits) {
+  const int HG = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const size_t entries = (size_t)batch * HG * splits * kHeadsPerGroup;
+  return entries * (kLat + 2) * sizeof(float);
+}
 
 hipError_t prepare_sparse_mla_decode() {
   return hipFuncSetAttribute((const void*)sparse_mla_decode_kernel,
@@ -300,8 +483,13 @@ hipError_t prepare_sparse_mla_decode() {
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  const int grid = ((batch + 7) / 8) * 8 * HG;
+  const int grid = batch * HG * p.splits;
   hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(grid), dim3(256), decode_lds_bytes(), stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)batch * p.heads * (kLat / 4);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -42,10 +42,11 @@ def _run_decode(dev_pool, locs_np, q, heads, max_top_k):
         hb.free()
 
 
-@pytest.mark.parametrize("B,H,k", [(5, 32, 77), (3, 16, 33), (2, 48, 64), (4, 128, 300)])
+@pytest.mark.parametrize("B,H,k", [(5, 32, 77), (3, 16, 33), (2, 48, 64), (4, 128, 300),
+                                   (3, 256, 100), (1, 128, 2048)])
 def test_decode_small_vs_oracle(B, H, k):
     print("[decode] B=%d H=%d k=%d" % (B, H, k), flush=True)
-    rows = 900
+    rows = max(900, k + 64)
     dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
     fill_host_rows_mla(dev, 31 + k, gen_device="cuda")
     rng = np.random.default_rng(k)
@@ -61,6 +62,34 @@ def test_decode_small_vs_oracle(B, H, k):
                                    dev.cpu().numpy(), float(np.float32(SCALE)))
     err = _normwise(got, ref)
     print("[decode] max normwise error %.3g" % err.max(), flush=True)
+    assert err.max() <= TOL
+
+
+def test_decode_score_far_above_the_first_block():
+    """One key in a late block scores far above everything in the first block
+    (a query aligned with that key's K vector), so the kernel's second pass
+    with a higher reference runs; the result must still match."""
+    print("[decode] second pass", flush=True)
+    B, H, k, rows = 2, 32, 2048, 3000
+    dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 77, gen_device="cuda")
+    rng = np.random.default_rng(9)
+    locs = rng.integers(0, rows, size=(B, k)).astype(np.int32)
+    # 2 rows -> 16 splits of 4 blocks; entry 453 is in the third block of a split
+    target = int(locs[0, 453])
+    # K vector of the target row in float (fp8 latent * scale ; bf16 rope)
+    row = dev[target].cpu()
+    lat = row[:512].view(torch.float8_e4m3fn).float()
+    sc = row[512:528].view(torch.float32)
+    kvec = torch.cat([lat * sc.repeat_interleave(128), row[528:656].view(torch.bfloat16).float()])
+    q = make_queries(B, H, seed=3, device="cuda").float().cpu()
+    q[0, :4] = 8.0 * kvec / kvec.abs().max()       # heads 0..3 of row 0 point at the target
+    q = q.to(torch.bfloat16).cuda().contiguous()
+    got = _run_decode(dev, locs, q, H, k)
+    ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16), locs,
+                                   dev.cpu().numpy(), float(np.float32(SCALE)))
+    err = _normwise(got, ref)
+    print("[decode] second pass max normwise error %.3g" % err.max(), flush=True)
     assert err.max() <= TOL
 
 
