@@ -434,10 +434,12 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch,
     pool->dec_ws = w;
     pool->dec_ws_bytes = need;
   }
+  // bf16 partial O, then fp32 (reference, denominator) per (row, group, split, head)
+  const size_t entries = need / (512 * sizeof(uint16_t) + 2 * sizeof(float));
   DecodeParams d;
   d.splits = splits;
-  d.part_o = (float*)pool->dec_ws;
-  d.part_ml = d.part_o + need / ((512 + 2) * sizeof(float)) * 512;
+  d.part_o = (uint16_t*)pool->dec_ws;
+  d.part_ml = (float*)(d.part_o + entries * 512);
   d.pool = pool->dev_ptrs[layer];
   d.pool_rows = pool->device_pool_rows;
   d.row_bytes = pool->cfg.row_bytes;

@@ -63,7 +63,7 @@ struct DecodeParams {
   const int32_t* locs;   // [batch][k]
   uint16_t* out;         // bf16 bits [batch][heads][512]
   int32_t splits;        // key splits per (batch row, 128-head group)
-  float* part_o;         // [batch][groups][splits][128][512] unnormalised O
+  uint16_t* part_o;      // bf16 [batch][groups][splits][128][512] O of a split / its denominator
   float* part_ml;        // [batch][groups][splits][128][2] reference (log2), denominator
 };
 

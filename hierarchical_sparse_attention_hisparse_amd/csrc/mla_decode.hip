@@ -30,9 +30,9 @@
 //    permuted consistently) are exchanged through LDS (one more barrier);
 //  - O^T += V^T P^T with the V^T fragments read from the same row-major tile
 //    with the LDS transpose load (ds_read_b64_tr_b16).
-// Each workgroup writes its unnormalised O with its reference and
-// denominator, and a second kernel combines the splits of a row and
-// normalises (the same algebra as one pass, in fp32).
+// Each workgroup writes its O normalised by its own denominator (bf16) with
+// its reference and denominator (fp32); a second kernel combines the splits
+// (the same algebra as one pass, in fp32).
 #include "common.h"
 #include "kernels.h"
 
@@ -398,37 +398,48 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
     __syncthreads();  // everyone has read the flag before it is cleared
   }
 
-  // Partial result of this split: unnormalised O (this wave's 128 dims of
-  // every head), and the reference (log2 units) and denominator of this
-  // wave's 32 heads.
+  // Partial result of this split, normalised by its own denominator: bf16
+  // O_j / l_j (this wave's 128 dims of every head), and fp32 reference (log2
+  // units) and denominator of this wave's 32 heads.  1/l crosses from the
+  // head's wave to the dims' waves through LDS.
   const int64_t e0 = ((int64_t)(b * HG + hg) * NS + sp) * kHeadsPerGroup;
-#pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht) {
-    float* po = p.part_o + (e0 + 16 * ht + r16) * kLat + 16 * kDimTilesPerWave * wave + 4 * g;
-#pragma unroll
-    for (int t = 0; t < kDimTilesPerWave; ++t) *(f32x4*)(po + 16 * t) = o[ht][t];
-  }
+  float* s_inv = (float*)smem;  // [128 heads]; the tiles are dead now
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     float l_tot = l_run[ht];
     l_tot += __shfl_xor(l_tot, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    const int64_t e = e0 + wave * kHeadsPerWave + 16 * ht + r16;
+    const int hl = wave * kHeadsPerWave + 16 * ht + r16;
     if (g == 0) {
-      p.part_ml[2 * e] = m_run[ht];
-      p.part_ml[2 * e + 1] = l_tot;
+      s_inv[hl] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      p.part_ml[2 * (e0 + hl)] = m_run[ht];
+      p.part_ml[2 * (e0 + hl) + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < kHeadTiles; ++ht) {
+    const float inv = s_inv[16 * ht + r16];
+    uint16_t* po = p.part_o + (e0 + 16 * ht + r16) * kLat + 16 * kDimTilesPerWave * wave + 4 * g;
+#pragma unroll
+    for (int t = 0; t < kDimTilesPerWave; ++t) {
+      uint2 w;
+      w.x = pack_bf16x2(o[ht][t][0] * inv, o[ht][t][1] * inv);
+      w.y = pack_bf16x2(o[ht][t][2] * inv, o[ht][t][3] * inv);
+      *(uint2*)(po + 16 * t) = w;
     }
   }
 }
 
-// Combine the splits of every (batch row, head): O = sum_j w_j O_j / sum_j w_j l_j
-// with w_j = 2^(m_j - max m).  One thread per 4 output dims.
+// Combine the splits of every (batch row, head): O = sum_j w_j l_j O_j /
+// sum_j w_j l_j with w_j = 2^(m_j - max m), O_j the normalised partials.
+// One thread per 8 output dims.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.batch * p.heads * (kLat / 4);
+  const int64_t total = (int64_t)p.batch * p.heads * (kLat / 8);
   if (idx >= total) return;
-  const int q = (int)(idx % (kLat / 4));
-  const int64_t bh = idx / (kLat / 4);
+  const int q = (int)(idx % (kLat / 8));
+  const int64_t bh = idx / (kLat / 8);
   const int h = (int)(bh % p.heads);
   const int b = (int)(bh / p.heads);
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
@@ -437,23 +448,31 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int64_t e0 = ((int64_t)(b * HG + hg) * NS) * kHeadsPerGroup + hl;
   float M = -INFINITY;
   for (int j = 0; j < NS; ++j) M = fmaxf(M, p.part_ml[2 * (e0 + (int64_t)j * kHeadsPerGroup)]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
     for (int j = 0; j < NS; ++j) {
       const int64_t e = e0 + (int64_t)j * kHeadsPerGroup;
       const float m = p.part_ml[2 * e];
       if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
-      L += w * p.part_ml[2 * e + 1];
-      acc += w * *(const f32x4*)(p.part_o + e * kLat + 4 * q);
+      const float wl = exp2f(m - M) * p.part_ml[2 * e + 1];
+      L += wl;
+      const uint4 v = *(const uint4*)(p.part_o + e * kLat + 8 * q);
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += wl * __uint_as_float(wd[k] << 16);
+        acc[2 * k + 1] += wl * __uint_as_float(wd[k] & 0xFFFF0000u);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint2 wv;
-  wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *(uint2*)(p.out + ((int64_t)b * p.heads + h) * kLat + 4 * q) = wv;
+  uint4 w;
+  w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *(uint4*)(p.out + ((int64_t)b * p.heads + h) * kLat + 8 * q) = w;
 }
 
 }  // namespace
@@ -472,7 +491,7 @@ int decode_splits(int batch, int heads, int k) {
 size_t decode_workspace_bytes(int batch, int heads, int splits) {
   const int HG = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
   const size_t entries = (size_t)batch * HG * splits * kHeadsPerGroup;
-  return entries * (kLat + 2) * sizeof(float);
+  return entries * (kLat * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t prepare_sparse_mla_decode() {
@@ -487,7 +506,7 @@ hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_
   hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(grid), dim3(256), decode_lds_bytes(), stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = (int64_t)batch * p.heads * (kLat / 4);
+  const int64_t total = (int64_t)batch * p.heads * (kLat / 8);
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();

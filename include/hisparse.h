@@ -222,12 +222,14 @@ int hisparse_gather_copy(hisparse_pool* pool, void* stream, int32_t batch,
  *   q_bf16   device bf16 [batch][heads][576]
  *   out_bf16 device bf16 [batch][heads][512]
  * Requires row_bytes >= 656, heads a multiple of 16, top_k <= max_top_k.
- * The keys of each row are split across workgroups and the partial results
- * combined by a second kernel; their fp32 workspace (about 257 KB per batch
+ * The keys of each row are split across workgroups and a second kernel
+ * combines the partial results; their workspace (about 129 KB per batch
  * row, 128-head group and split, with up to 256 / (batch * groups) splits)
  * is allocated by the pool on the first call that needs more than it holds:
  * that call synchronises the device, later calls of the same or a smaller
- * shape allocate nothing.  Errors: EINVAL, EUNSUPPORTED, ENOMEM, EHIP.
+ * shape allocate nothing.  Calls on one pool that overlap in time (different
+ * streams) race on this workspace.  Errors: EINVAL, EUNSUPPORTED, ENOMEM,
+ * EHIP.
  */
 int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream,
                                int32_t batch, int32_t heads, int32_t top_k,

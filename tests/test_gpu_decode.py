@@ -93,6 +93,38 @@ def test_decode_score_far_above_the_first_block():
     assert err.max() <= TOL
 
 
+def test_decode_repeated_calls_on_one_pool():
+    """Calls of different shapes on one pool: the split workspace grows and
+    the arrival counters are left at zero for the next call."""
+    print("[decode] repeated calls", flush=True)
+    rows = 1200
+    dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 5, gen_device="cuda")
+    hb = hs.HostBuffer(656 * 16)
+    cfg = hs.PoolConfig(max_requests=1, slots=1024, max_top_k=1024, max_batch=8, max_seq_len=16)
+    pool = hs.hisparse_init_pool(cfg, [hb], [16], [dev], rows)
+    try:
+        for call, (B, H, k) in enumerate([(2, 128, 300), (7, 128, 1000), (2, 128, 300), (5, 256, 64),
+                                          (7, 128, 1000)]):
+            rng = np.random.default_rng(100 + call)
+            locs = rng.integers(-1, rows, size=(B, k)).astype(np.int32)
+            q = make_queries(B, H, seed=call, device="cuda")
+            out = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+            hs.hisparse_sparse_mla_decode(pool, None, B, H, k, 0, q, torch.from_numpy(locs).cuda(),
+                                          SCALE, out)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy().astype(np.float64)
+            ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16), locs,
+                                           dev.cpu().numpy(), float(np.float32(SCALE)))
+            err = _normwise(got, ref)
+            print("[decode] call %d B=%d H=%d k=%d max normwise error %.3g" % (call, B, H, k, err.max()),
+                  flush=True)
+            assert err.max() <= TOL
+    finally:
+        hs.hisparse_destroy_pool(pool)
+        hb.free()
+
+
 def test_decode_all_invalid_gives_zero():
     dev = torch.empty((64, 656), dtype=torch.uint8, device="cuda")
     fill_host_rows_mla(dev, 3, gen_device="cuda")
