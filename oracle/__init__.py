@@ -9,6 +9,9 @@ from .oracle import (  # noqa: F401
     OracleState,
     oracle_resolve,
     oracle_sparse_mla_decode,
+    oracle_mirror_rows,
+    oracle_invalidate_tokens,
+    oracle_invalidate_host_rows,
     e4m3_to_double,
     bf16_to_double,
 )

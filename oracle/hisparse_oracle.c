@@ -379,3 +379,113 @@ int oracle_sparse_mla_decode(int32_t batch, int32_t heads, int32_t top_k,
   free(z);
   return OR_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Row mirror (eager backup) and hot-entry invalidation.                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * oracle_mirror_rows -- copy device rows back to host rows in layers
+ * [layer_begin, layer_end): host_pool[l][host_rows[i]] = dev_pool[l][dev_rows[i]].
+ *
+ * Follows the per-step flow of [P2] (step 5: the row written by the
+ * previous token is copied from the device back to the host pool) and the
+ * row mirror of [P3] section 6 (rows written by the forward pass are
+ * mirrored to their host rows, so that a later spill moves no data).
+ * Readings: an entry whose device row is negative is padding (skipped, not
+ * counted); a device row >= dev_pool_rows or a host row outside
+ * [0, host_pool_rows[l]) skips that layer's copy and counts one tripwire.
+ * With `validate`, two copied entries naming one host row are rejected.
+ */
+int oracle_mirror_rows(int32_t row_bytes, int32_t count, const int32_t* dev_rows,
+                       const int64_t* host_rows, uint8_t* const* dev_pools,
+                       int64_t dev_pool_rows, uint8_t* const* host_pools,
+                       const int64_t* host_pool_rows, int32_t layer_begin, int32_t layer_end,
+                       uint64_t* stats, int validate) {
+  if (row_bytes <= 0 || count < 0 || layer_begin < 0 || layer_end < layer_begin) return OR_EINVAL;
+  if (validate) {
+    for (int32_t i = 0; i < count; ++i)
+      for (int32_t j = i + 1; j < count; ++j)
+        if (dev_rows[i] >= 0 && dev_rows[j] >= 0 && host_rows[i] == host_rows[j]) return OR_EINVAL;
+  }
+  for (int32_t l = layer_begin; l < layer_end; ++l) {
+    for (int32_t i = 0; i < count; ++i) {
+      const int32_t d = dev_rows[i];
+      const int64_t h = host_rows[i];
+      if (d < 0) continue;
+      if ((int64_t)d >= dev_pool_rows || h < 0 || h >= host_pool_rows[l]) {
+        stats[ST_TRIP] += 1;
+        continue;
+      }
+      memcpy(host_pools[l] + h * row_bytes, dev_pools[l] + (int64_t)d * row_bytes,
+             (size_t)row_bytes);
+    }
+  }
+  return OR_OK;
+}
+
+/*
+ * oracle_invalidate_tokens -- for each entry i, clear every hot slot of
+ * request row req_rows[i] whose token lies in [tok_begin[i], tok_end[i]):
+ * the slot becomes empty (token -1) with stamp 0, the state of a slot that
+ * was never used.  Follows the precise clearing of rows rewritten by a
+ * prefill in [P3] section 6 (hot-cache coherence); with the hot key being
+ * the token position, "rewritten rows" are token ranges of a request.
+ * Readings: req_rows[i] < 0 is padding; req_rows[i] >= R counts one
+ * tripwire and clears nothing; an empty range clears nothing.
+ */
+int oracle_invalidate_tokens(int32_t R, int32_t S, int32_t count, const int32_t* req_rows,
+                             const int32_t* tok_begin, const int32_t* tok_end,
+                             int32_t* slot_tokens, int32_t* lru_slots, uint64_t* stats) {
+  if (R <= 0 || S <= 0 || count < 0) return OR_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t r = req_rows[i];
+    if (r < 0) continue;
+    if (r >= R) {
+      stats[ST_TRIP] += 1;
+      continue;
+    }
+    for (int32_t s = 0; s < S; ++s) {
+      const int32_t t = slot_tokens[(int64_t)r * S + s];
+      if (t >= tok_begin[i] && t < tok_end[i]) {
+        slot_tokens[(int64_t)r * S + s] = -1;
+        lru_slots[(int64_t)r * S + s] = 0;
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/*
+ * oracle_invalidate_host_rows -- clear every hot slot (of every request row)
+ * holding a token whose host row host_cache_locs[r][t] is one of the
+ * `count` rows in `rows` (host rows that were reused for other content or
+ * rewritten): token -1, stamp 0.  Follows [P3] section 6 (hot-cache
+ * coherence: newly allocated host blocks are matched in a batch against the
+ * hot entries, which must be cleared when their host rows are reused).
+ * Tokens outside [0, max_seq_len) (empty or corrupted slots) are left alone.
+ * With `validate`, `rows` must be sorted ascending (the form the kernel
+ * searches).  Plain linear membership test.
+ */
+int oracle_invalidate_host_rows(int32_t R, int32_t S, int64_t max_seq_len, int32_t count,
+                                const int64_t* rows, const int64_t* host_cache_locs,
+                                int32_t* slot_tokens, int32_t* lru_slots, int validate) {
+  if (R <= 0 || S <= 0 || count < 0 || max_seq_len <= 0) return OR_EINVAL;
+  if (validate)
+    for (int32_t i = 1; i < count; ++i)
+      if (rows[i] < rows[i - 1]) return OR_EINVAL;
+  for (int32_t r = 0; r < R; ++r) {
+    for (int32_t s = 0; s < S; ++s) {
+      const int32_t t = slot_tokens[(int64_t)r * S + s];
+      if (t < 0 || (int64_t)t >= max_seq_len) continue;
+      const int64_t h = host_cache_locs[(int64_t)r * max_seq_len + t];
+      int found = 0;
+      for (int32_t i = 0; i < count && !found; ++i) found = rows[i] == h;
+      if (found) {
+        slot_tokens[(int64_t)r * S + s] = -1;
+        lru_slots[(int64_t)r * S + s] = 0;
+      }
+    }
+  }
+  return OR_OK;
+}

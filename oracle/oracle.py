@@ -46,6 +46,12 @@ def load_oracle():
     lib.oracle_sparse_mla_decode.restype = ctypes.c_int
     lib.oracle_sparse_mla_decode.argtypes = [i32, i32, i32, P, P, P, i64, i32,
                                              ctypes.c_float, P]
+    lib.oracle_mirror_rows.restype = ctypes.c_int
+    lib.oracle_mirror_rows.argtypes = [i32, i32, P, P, P, i64, P, P, i32, i32, P, ctypes.c_int]
+    lib.oracle_invalidate_tokens.restype = ctypes.c_int
+    lib.oracle_invalidate_tokens.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_invalidate_host_rows.restype = ctypes.c_int
+    lib.oracle_invalidate_host_rows.argtypes = [i32, i32, i64, i32, P, P, P, P, ctypes.c_int]
     lib.oracle_e4m3_to_double.restype = ctypes.c_double
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
@@ -158,3 +164,49 @@ def e4m3_to_double(code: int) -> float:
 
 def bf16_to_double(bits: int) -> float:
     return load_oracle().oracle_bf16_to_double(bits)
+
+
+def oracle_mirror_rows(state: OracleState, *, dev_rows, host_rows, host_pools, host_pool_rows,
+                       layer_begin: int = 0, layer_end=None, validate: bool = False):
+    """Copy the oracle's device rows ``dev_rows`` to ``host_rows`` of the host
+    pools (numpy arrays or CPU tensors, modified in place) in each layer."""
+    lib = load_oracle()
+    dev_rows = np.ascontiguousarray(dev_rows, dtype=np.int32)
+    host_rows = np.ascontiguousarray(host_rows, dtype=np.int64)
+    assert dev_rows.shape == host_rows.shape
+    layer_end = state.L if layer_end is None else layer_end
+    hp = (ctypes.c_void_p * state.L)(*[int(_host_addr(h)) for h in host_pools])
+    dp = (ctypes.c_void_p * state.L)(*[d.ctypes.data for d in state.dev_pools])
+    hrows = np.ascontiguousarray(host_pool_rows, dtype=np.int64)
+    rc = lib.oracle_mirror_rows(state.row_bytes, len(dev_rows), _ptr(dev_rows), _ptr(host_rows),
+                                ctypes.cast(dp, ctypes.c_void_p), state.dev_pool_rows,
+                                ctypes.cast(hp, ctypes.c_void_p), _ptr(hrows), layer_begin,
+                                layer_end, _ptr(state.stats), 1 if validate else 0)
+    if rc != 0:
+        raise ValueError("oracle_mirror_rows rejected its input (code %d)" % rc)
+
+
+def oracle_invalidate_tokens(state: OracleState, *, req_rows, tok_begin, tok_end):
+    """Clear the hot slots of the given request rows holding tokens in the ranges."""
+    lib = load_oracle()
+    req_rows = np.ascontiguousarray(req_rows, dtype=np.int32)
+    tok_begin = np.ascontiguousarray(tok_begin, dtype=np.int32)
+    tok_end = np.ascontiguousarray(tok_end, dtype=np.int32)
+    rc = lib.oracle_invalidate_tokens(state.R, state.S, len(req_rows), _ptr(req_rows),
+                                      _ptr(tok_begin), _ptr(tok_end), _ptr(state.slot_tokens),
+                                      _ptr(state.lru_slots), _ptr(state.stats))
+    if rc != 0:
+        raise ValueError("oracle_invalidate_tokens rejected its input (code %d)" % rc)
+
+
+def oracle_invalidate_host_rows(state: OracleState, *, rows, host_cache_locs, max_seq_len: int,
+                                validate: bool = False):
+    """Clear every hot slot whose token's host row is in ``rows`` (sorted)."""
+    lib = load_oracle()
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    host_cache_locs = np.ascontiguousarray(host_cache_locs, dtype=np.int64)
+    rc = lib.oracle_invalidate_host_rows(state.R, state.S, max_seq_len, len(rows), _ptr(rows),
+                                         _ptr(host_cache_locs), _ptr(state.slot_tokens),
+                                         _ptr(state.lru_slots), 1 if validate else 0)
+    if rc != 0:
+        raise ValueError("oracle_invalidate_host_rows rejected its input (code %d)" % rc)
