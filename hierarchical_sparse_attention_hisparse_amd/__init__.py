@@ -18,7 +18,10 @@ from ._binding import (  # noqa: F401
     hisparse_host_alloc,
     hisparse_host_free,
     hisparse_init_pool,
+    hisparse_invalidate_host_rows,
+    hisparse_invalidate_tokens,
     hisparse_last_error,
+    hisparse_mirror_rows,
     hisparse_resolve,
     hisparse_resolve_plan,
     hisparse_sparse_mla_decode,

@@ -82,6 +82,12 @@ def load_library():
     lib.hisparse_resolve_plan.argtypes = resolve_args
     lib.hisparse_gather_copy.restype = I
     lib.hisparse_gather_copy.argtypes = [V, V, I32, I32, I32, V]
+    lib.hisparse_mirror_rows.restype = ctypes.c_int
+    lib.hisparse_mirror_rows.argtypes = [V, V, I32, V, V, I32, I32, V]
+    lib.hisparse_invalidate_tokens.restype = ctypes.c_int
+    lib.hisparse_invalidate_tokens.argtypes = [V, V, I32, V, V, V, V, V, V]
+    lib.hisparse_invalidate_host_rows.restype = ctypes.c_int
+    lib.hisparse_invalidate_host_rows.argtypes = [V, V, I32, V, V, V, V]
     lib.hisparse_sparse_mla_decode.restype = I
     lib.hisparse_sparse_mla_decode.argtypes = [V, V, I32, I32, I32, I32, V, V,
                                                ctypes.c_float, V]
@@ -261,6 +267,54 @@ def hisparse_gather_copy(pool, stream, batch, layer_begin=0, layer_end=None, sta
     _check_rc(load_library().hisparse_gather_copy(pool.handle, _stream_handle(stream), batch,
                                                   layer_begin, layer_end, sp),
               "hisparse_gather_copy")
+
+
+def hisparse_mirror_rows(pool, stream, dev_rows, host_rows, layer_begin=0, layer_end=None,
+                         stats=None):
+    """Copy device rows ``dev_rows`` (int32 [n]) to host rows ``host_rows``
+    (int64 [n]) of every layer in [layer_begin, layer_end)."""
+    import torch
+    if layer_end is None:
+        layer_end = pool.cfg.num_layers
+    n = int(dev_rows.shape[0])
+    dp = _dev(dev_rows, torch.int32, (n,), "dev_rows")
+    hp = _dev(host_rows, torch.int64, (n,), "host_rows")
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    _check_rc(load_library().hisparse_mirror_rows(pool.handle, _stream_handle(stream), n, dp, hp,
+                                                  layer_begin, layer_end, sp),
+              "hisparse_mirror_rows")
+
+
+def hisparse_invalidate_tokens(pool, stream, req_rows, tok_begin, tok_end, slot_tokens,
+                               lru_slots, stats=None):
+    """Empty the hot slots of ``req_rows`` holding tokens in [tok_begin, tok_end)."""
+    import torch
+    n = int(req_rows.shape[0])
+    R, S = pool.cfg.max_requests, pool.cfg.slots
+    rp = _dev(req_rows, torch.int32, (n,), "req_rows")
+    bp = _dev(tok_begin, torch.int32, (n,), "tok_begin")
+    ep = _dev(tok_end, torch.int32, (n,), "tok_end")
+    stp = _dev(slot_tokens, torch.int32, (R, S), "slot_tokens")
+    lp = _dev(lru_slots, torch.int32, (R, S), "lru_slots")
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    _check_rc(load_library().hisparse_invalidate_tokens(pool.handle, _stream_handle(stream), n, rp,
+                                                        bp, ep, stp, lp, sp),
+              "hisparse_invalidate_tokens")
+
+
+def hisparse_invalidate_host_rows(pool, stream, rows_sorted, host_cache_locs, slot_tokens,
+                                  lru_slots):
+    """Empty every hot slot whose token's host row is in ``rows_sorted``."""
+    import torch
+    n = int(rows_sorted.shape[0])
+    R, S = pool.cfg.max_requests, pool.cfg.slots
+    rp = _dev(rows_sorted, torch.int64, (n,), "rows_sorted")
+    lp_ = _dev(host_cache_locs, torch.int64, (R, pool.cfg.max_seq_len), "host_cache_locs")
+    stp = _dev(slot_tokens, torch.int32, (R, S), "slot_tokens")
+    lp = _dev(lru_slots, torch.int32, (R, S), "lru_slots")
+    _check_rc(load_library().hisparse_invalidate_host_rows(pool.handle, _stream_handle(stream), n,
+                                                           rp, lp_, stp, lp),
+              "hisparse_invalidate_host_rows")
 
 
 def hisparse_sparse_mla_decode(pool, stream, batch, heads, top_k, layer, q_bf16,

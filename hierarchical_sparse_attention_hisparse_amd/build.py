@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhisparse.so")
-SOURCES = ["abi.hip", "resolve.hip", "gather.hip", "mla_decode.hip"]
+SOURCES = ["abi.hip", "resolve.hip", "gather.hip", "mla_decode.hip", "maintain.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

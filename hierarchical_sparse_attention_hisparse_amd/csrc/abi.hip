@@ -313,6 +313,7 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   if (e == hipSuccess) e = hipMemcpy(pool->d_host_rows, host_pool_rows, bytes_tab, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = prepare_resolve(kLdsBudget);
   if (e == hipSuccess) e = prepare_sparse_mla_decode();
+  if (e == hipSuccess) e = prepare_maintain();
   if (e != hipSuccess) {
     (void)hipFree(ws);
     free(pool->host_rows);
@@ -391,6 +392,95 @@ int hisparse_resolve(hisparse_pool* pool, void* stream, int32_t batch, int32_t t
   if (rc != HISPARSE_OK || fuse) return rc == HISPARSE_OK ? ok() : rc;
   rc = launch_copy(pool, (hipStream_t)stream, batch, 0, pool->cfg.num_layers, stats);
   return rc == HISPARSE_OK ? ok() : rc;
+}
+
+int hisparse_mirror_rows(hisparse_pool* pool, void* stream, int32_t count, const int32_t* dev_rows,
+                         const int64_t* host_rows, int32_t layer_begin, int32_t layer_end,
+                         uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  if (count < 0) return fail(HISPARSE_EINVAL, "count %d < 0", count);
+  if (layer_begin < 0 || layer_end > pool->cfg.num_layers || layer_begin > layer_end)
+    return fail(HISPARSE_EINVAL, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
+                pool->cfg.num_layers);
+  if (count == 0 || layer_begin == layer_end) return ok();
+  if (!dev_rows || !host_rows) return fail(HISPARSE_EINVAL, "dev_rows and host_rows must not be NULL");
+  if (!aligned(dev_rows, 4) || !aligned(host_rows, 8))
+    return fail(HISPARSE_EINVAL, "dev_rows / host_rows are not aligned to their element size");
+  if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  MirrorParams m;
+  m.dev_rows = dev_rows;
+  m.host_rows = host_rows;
+  m.count = count;
+  m.units = pool->cfg.row_bytes / 16;
+  m.layer_begin = layer_begin;
+  m.dev_pool_rows = pool->device_pool_rows;
+  m.dev_pools = pool->d_dev_ptrs;
+  m.host_pools = pool->d_host_ptrs;
+  m.host_rows_of_layer = pool->d_host_rows;
+  m.stats = (unsigned long long*)stats;
+  hipError_t e = launch_mirror_rows(m, layer_end - layer_begin, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "row mirror kernel launch");
+  return ok();
+}
+
+int hisparse_invalidate_tokens(hisparse_pool* pool, void* stream, int32_t count,
+                               const int32_t* req_rows, const int32_t* tok_begin,
+                               const int32_t* tok_end, int32_t* slot_tokens, int32_t* lru_slots,
+                               uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  if (count < 0) return fail(HISPARSE_EINVAL, "count %d < 0", count);
+  if (count == 0) return ok();
+  if (!req_rows || !tok_begin || !tok_end || !slot_tokens || !lru_slots)
+    return fail(HISPARSE_EINVAL, "array arguments must not be NULL");
+  if (!aligned(req_rows, 4) || !aligned(tok_begin, 4) || !aligned(tok_end, 4) ||
+      !aligned(slot_tokens, 4) || !aligned(lru_slots, 4))
+    return fail(HISPARSE_EINVAL, "int32 arrays must be 4-byte aligned");
+  if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  InvalidateParams v = {};
+  v.R = pool->cfg.max_requests;
+  v.S = pool->cfg.slots;
+  v.max_seq_len = pool->cfg.max_seq_len;
+  v.count = count;
+  v.req_rows = req_rows;
+  v.tok_begin = tok_begin;
+  v.tok_end = tok_end;
+  v.slot_tokens = slot_tokens;
+  v.lru_slots = lru_slots;
+  v.stats = (unsigned long long*)stats;
+  hipError_t e = launch_invalidate_tokens(v, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "token invalidation kernel launch");
+  return ok();
+}
+
+int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t count,
+                                  const int64_t* rows_sorted, const int64_t* host_cache_locs,
+                                  int32_t* slot_tokens, int32_t* lru_slots) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  if (count < 0) return fail(HISPARSE_EINVAL, "count %d < 0", count);
+  if (count == 0) return ok();
+  if (!rows_sorted || !host_cache_locs || !slot_tokens || !lru_slots)
+    return fail(HISPARSE_EINVAL, "array arguments must not be NULL");
+  if (!aligned(rows_sorted, 8) || !aligned(host_cache_locs, 8) || !aligned(slot_tokens, 4) ||
+      !aligned(lru_slots, 4))
+    return fail(HISPARSE_EINVAL, "arrays are not aligned to their element size");
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  InvalidateParams v = {};
+  v.R = pool->cfg.max_requests;
+  v.S = pool->cfg.slots;
+  v.max_seq_len = pool->cfg.max_seq_len;
+  v.count = count;
+  v.rows = rows_sorted;
+  v.host_cache_locs = host_cache_locs;
+  v.slot_tokens = slot_tokens;
+  v.lru_slots = lru_slots;
+  hipError_t e = launch_invalidate_host_rows(v, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "host-row invalidation kernel launch");
+  return ok();
 }
 
 int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,

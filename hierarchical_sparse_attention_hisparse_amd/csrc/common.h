@@ -36,6 +36,9 @@ constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
 constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
 constexpr int kCopyRowsInFlight = 4;  // rows per wavefront per iteration of the fused copy
 
+// Invalidation by host rows: sets up to this many rows are searched in LDS.
+constexpr int kInvalidateLdsRows = 8192;
+
 // Decode: at most this many key splits per (batch row, head group).
 constexpr int kMaxDecodeSplits = 16;
 

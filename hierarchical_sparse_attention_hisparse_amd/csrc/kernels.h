@@ -67,12 +67,43 @@ struct DecodeParams {
   float* part_ml;        // [batch][groups][splits][128][2] reference (log2), denominator
 };
 
+struct MirrorParams {
+  const int32_t* dev_rows;           // [count]
+  const int64_t* host_rows;          // [count]
+  int32_t count;
+  int32_t units;                     // row_bytes / 16
+  int32_t layer_begin;
+  int64_t dev_pool_rows;
+  const unsigned char* const* dev_pools;  // device array [L]
+  unsigned char* const* host_pools;       // device array [L] of device-mapped host pointers
+  const int64_t* host_rows_of_layer;      // device array [L]
+  unsigned long long* stats;              // may be null
+};
+
+struct InvalidateParams {
+  int32_t R, S;
+  int64_t max_seq_len;
+  int32_t count;
+  const int32_t* req_rows;   // token ranges: [count]
+  const int32_t* tok_begin;
+  const int32_t* tok_end;
+  const int64_t* rows;       // host rows: [count], sorted ascending
+  const int64_t* host_cache_locs;
+  int32_t* slot_tokens;
+  int32_t* lru_slots;
+  unsigned long long* stats;  // may be null
+};
+
 hipError_t prepare_resolve(size_t lds_bytes);
 hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream);
 hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream);
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
 hipError_t prepare_sparse_mla_decode();
 size_t decode_lds_bytes();
+hipError_t launch_mirror_rows(const MirrorParams& p, int layers, hipStream_t stream);
+hipError_t launch_invalidate_tokens(const InvalidateParams& p, hipStream_t stream);
+hipError_t launch_invalidate_host_rows(const InvalidateParams& p, hipStream_t stream);
+hipError_t prepare_maintain();
 int decode_splits(int batch, int heads, int k);
 size_t decode_workspace_bytes(int batch, int heads, int splits);
 

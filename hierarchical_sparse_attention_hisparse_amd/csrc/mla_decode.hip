@@ -49,7 +49,6 @@ constexpr int kDecWaves = 4;
 constexpr int kHeadsPerWave = 32;
 constexpr int kHeadsPerGroup = kDecWaves * kHeadsPerWave;  // 128
 constexpr float kMaxExcessLog2 = 64.f;            // largest score above a head's reference (log2)
-constexpr int kRope = kDim - kLat;                // 64
 constexpr int kQRopeStrideBytes = 144;            // 64 bf16 + 16 pad: conflict-free b128 reads
 constexpr int kLatSteps = kLat / 32;              // 16 k-steps over the latent
 constexpr int kQKAhead = 2;                       // LDS reads this many MFMA steps ahead

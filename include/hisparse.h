@@ -237,6 +237,60 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream,
                                const int32_t* device_buffer_locs,
                                float softmax_scale, void* out_bf16);
 
+/*
+ * hisparse_mirror_rows -- the row mirror (eager backup): copy device rows
+ * back to their host rows in layers [layer_begin, layer_end):
+ *   host_pool[l][host_rows[i]] = device_pool[l][dev_rows[i]], i < count.
+ * This is the last step of a decode step in the per-step flow of the
+ * gogongxt.com HiSparse page (the previous token's row goes back to the
+ * host), and the row mirror of "vLLM Hybrid HiSparse 源码实现分析" section 6
+ * (rows written by the forward pass are mirrored so that a later spill
+ * moves no data).  It keeps "every token t < seq_len has its host row" true
+ * in a running decode loop.
+ *   dev_rows[count]   device int32: device pool rows; < 0 = padding entry
+ *                     (skipped, not counted)
+ *   host_rows[count]  device int64: destination host rows
+ *   stats             device uint64[5] or NULL: stats[4] += 1 per layer for
+ *                     a device row >= device_pool_rows or a host row
+ *                     outside [0, host_pool_rows[l]) (that copy is skipped)
+ * Destinations must be distinct (if not, which copy lands is unspecified;
+ * memory stays safe).  Stream-ordered, no readback.  Errors: EINVAL, EHIP.
+ */
+int hisparse_mirror_rows(hisparse_pool* pool, void* stream, int32_t count,
+                         const int32_t* dev_rows, const int64_t* host_rows,
+                         int32_t layer_begin, int32_t layer_end, uint64_t* stats);
+
+/*
+ * hisparse_invalidate_tokens -- for each entry i < count, empty every hot
+ * slot of request row req_rows[i] holding a token in
+ * [tok_begin[i], tok_end[i]): slot_tokens = -1, lru_slots = 0 (the state of
+ * a never-used slot, first in victim order).  The precise clearing of rows
+ * rewritten by a prefill ("vLLM Hybrid HiSparse 源码实现分析" section 6, hot-
+ * cache coherence); with [0, INT32_MAX) it clears a request row that is
+ * handed to a new request.  All arrays are device int32 of length count
+ * except the state ([R][S]).  req_rows[i] < 0 is padding; >= R counts one
+ * tripwire in stats[4] (stats may be NULL).  Errors: EINVAL, EHIP.
+ */
+int hisparse_invalidate_tokens(hisparse_pool* pool, void* stream, int32_t count,
+                               const int32_t* req_rows, const int32_t* tok_begin,
+                               const int32_t* tok_end, int32_t* slot_tokens,
+                               int32_t* lru_slots, uint64_t* stats);
+
+/*
+ * hisparse_invalidate_host_rows -- empty every hot slot, of every request
+ * row, whose token t maps to a host row host_cache_locs[r][t] in the set
+ * rows_sorted[count] (device int64, ascending): host rows that were reused
+ * for other content or rewritten ("vLLM Hybrid HiSparse 源码实现分析"
+ * section 6: newly allocated host blocks are matched in a batch against
+ * the hot entries).  Slots with tokens outside [0, max_seq_len) are left
+ * alone.  The set is binary-searched, in LDS when it holds at most 8192
+ * rows; an unsorted set gives an unspecified (memory-safe) result.
+ * Errors: EINVAL, EHIP.
+ */
+int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t count,
+                                  const int64_t* rows_sorted, const int64_t* host_cache_locs,
+                                  int32_t* slot_tokens, int32_t* lru_slots);
+
 /* Free the pool's workspace and the pool.  NULL is a no-op.  The caller must
  * make sure no work that uses the pool is still queued. */
 void hisparse_destroy_pool(hisparse_pool* pool);

@@ -44,10 +44,11 @@ class Workload:
     seed: int = 0
     row_bytes: int = ROW_BYTES
     meta: dict = field(default_factory=dict)
+    extra_dev_rows: int = 0     # device rows after the hot and resident rows (staging)
 
     @property
     def dev_pool_rows(self) -> int:
-        return self.R * self.S + self.resident_pages * self.P
+        return self.R * self.S + self.resident_pages * self.P + self.extra_dev_rows
 
     @property
     def max_pages(self) -> int:
