@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     STAT_NAMES,
     hisparse_destroy_pool,
     hisparse_gather_copy,
+    hisparse_gather_copy_step,
     hisparse_host_alloc,
     hisparse_host_free,
     hisparse_init_pool,
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     hisparse_mirror_rows,
     hisparse_resolve,
     hisparse_resolve_plan,
+    hisparse_resolve_steps,
     hisparse_sparse_mla_decode,
     library_path,
     load_library,

@@ -27,7 +27,7 @@ class _Config(ctypes.Structure):
         ("max_requests", ctypes.c_int32), ("slots", ctypes.c_int32),
         ("max_top_k", ctypes.c_int32), ("max_batch", ctypes.c_int32),
         ("row_bytes", ctypes.c_int32), ("num_layers", ctypes.c_int32),
-        ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_steps", ctypes.c_int32),
         ("resident_pages", ctypes.c_int64), ("max_seq_len", ctypes.c_int64),
     ]
 
@@ -43,10 +43,11 @@ class PoolConfig:
     page_size: int = 0
     resident_pages: int = 0
     max_seq_len: int = 0
+    max_steps: int = 1
 
     def _c(self) -> _Config:
         return _Config(self.max_requests, self.slots, self.max_top_k, self.max_batch,
-                       self.row_bytes, self.num_layers, self.page_size, 0,
+                       self.row_bytes, self.num_layers, self.page_size, self.max_steps,
                        self.resident_pages, self.max_seq_len)
 
 
@@ -82,6 +83,10 @@ def load_library():
     lib.hisparse_resolve_plan.argtypes = resolve_args
     lib.hisparse_gather_copy.restype = I
     lib.hisparse_gather_copy.argtypes = [V, V, I32, I32, I32, V]
+    lib.hisparse_resolve_steps.restype = ctypes.c_int
+    lib.hisparse_resolve_steps.argtypes = [V, V, I32] + resolve_args[2:]
+    lib.hisparse_gather_copy_step.restype = ctypes.c_int
+    lib.hisparse_gather_copy_step.argtypes = [V, V, I32, I32, I32, I32, V]
     lib.hisparse_mirror_rows.restype = ctypes.c_int
     lib.hisparse_mirror_rows.argtypes = [V, V, I32, V, V, I32, I32, V]
     lib.hisparse_invalidate_tokens.restype = ctypes.c_int
@@ -217,24 +222,49 @@ def hisparse_destroy_pool(pool: _Pool):
 
 def _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
                   resident_block_table, slot_tokens, lru_slots, lru_clock,
-                  device_buffer_locs, stats):
+                  device_buffer_locs, stats, steps=None):
     import torch
     c = pool.cfg
     R, S = c.max_requests, c.slots
     max_pages = (c.max_seq_len + c.page_size - 1) // c.page_size if c.page_size > 0 else 0
+    lead = () if steps is None else (steps,)
     return [
         _dev(req_idx, torch.int32, (batch,), "req_idx"),
-        _dev(top_k_tokens, torch.int32, (batch, top_k), "top_k_tokens"),
-        _dev(seq_lens, torch.int32, (batch,), "seq_lens"),
+        _dev(top_k_tokens, torch.int32, lead + (batch, top_k), "top_k_tokens"),
+        _dev(seq_lens, torch.int32, lead + (batch,), "seq_lens"),
         _dev(host_cache_locs, torch.int64, (R, c.max_seq_len), "host_cache_locs"),
         _dev(resident_block_table, torch.int32, (R, max_pages), "resident_block_table",
              allow_none=True),
         _dev(slot_tokens, torch.int32, (R, S), "slot_tokens"),
         _dev(lru_slots, torch.int32, (R, S), "lru_slots"),
         _dev(lru_clock, torch.int32, (R,), "lru_clock"),
-        _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs"),
+        _dev(device_buffer_locs, torch.int32, lead + (batch, top_k), "device_buffer_locs"),
         _dev(stats, torch.int64, (5,), "stats", allow_none=True),
     ]
+
+
+def hisparse_resolve_steps(pool, stream, steps, batch, top_k, req_idx, top_k_tokens, seq_lens,
+                           host_cache_locs, resident_block_table, slot_tokens, lru_slots,
+                           lru_clock, device_buffer_locs, stats=None):
+    """The verification steps of one speculative decode step: top_k_tokens
+    [steps, batch, top_k], seq_lens [steps, batch], device_buffer_locs
+    [steps, batch, top_k]."""
+    ptrs = _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,
+                         resident_block_table, slot_tokens, lru_slots, lru_clock,
+                         device_buffer_locs, stats, steps=steps)
+    _check_rc(load_library().hisparse_resolve_steps(pool.handle, _stream_handle(stream), steps,
+                                                    batch, top_k, *ptrs), "hisparse_resolve_steps")
+
+
+def hisparse_gather_copy_step(pool, stream, step, batch, layer_begin=0, layer_end=None,
+                              stats=None):
+    import torch
+    if layer_end is None:
+        layer_end = pool.cfg.num_layers
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    _check_rc(load_library().hisparse_gather_copy_step(pool.handle, _stream_handle(stream), step,
+                                                       batch, layer_begin, layer_end, sp),
+              "hisparse_gather_copy_step")
 
 
 def hisparse_resolve(pool, stream, batch, top_k, req_idx, top_k_tokens, seq_lens,

@@ -103,7 +103,7 @@ int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
                 const int32_t* req_idx, const int32_t* top_k_tokens, const int32_t* seq_lens,
                 const int64_t* host_cache_locs, const int32_t* bt, int32_t* slot_tokens,
                 int32_t* lru_slots, int32_t* lru_clock, int32_t* out, uint64_t* stats,
-                int32_t copy_layers) {
+                int32_t copy_layers, int32_t slice = 0) {
   ResolveParams p;
   p.R = pool->cfg.max_requests;
   p.S = pool->cfg.slots;
@@ -122,9 +122,10 @@ int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   p.clk = lru_clock;
   p.out = out;
   p.stats = (unsigned long long*)stats;
-  p.plan_src = pool->plan_src;
-  p.plan_dst = pool->plan_dst;
-  p.plan_cnt = pool->plan_cnt;
+  const size_t slice_entries = (size_t)pool->cfg.max_batch * pool->cfg.max_top_k;
+  p.plan_src = pool->plan_src + slice * slice_entries;
+  p.plan_dst = pool->plan_dst + slice * slice_entries;
+  p.plan_cnt = pool->plan_cnt + (size_t)slice * pool->cfg.max_batch;
   p.plan_stride = pool->cfg.max_top_k;
   for (int l = 0; l < kMaxFusedLayers; ++l) {
     const bool have = l < copy_layers;
@@ -147,14 +148,15 @@ int copy_chunks_for(int batch) {
 }
 
 int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t lb, int32_t le,
-                uint64_t* stats) {
+                uint64_t* stats, int32_t slice = 0) {
   CopyParams c;
   c.host_pools = pool->d_host_ptrs;
   c.dev_pools = pool->d_dev_ptrs;
   c.host_rows = pool->d_host_rows;
-  c.plan_src = pool->plan_src;
-  c.plan_dst = pool->plan_dst;
-  c.plan_cnt = pool->plan_cnt;
+  const size_t slice_entries = (size_t)pool->cfg.max_batch * pool->cfg.max_top_k;
+  c.plan_src = pool->plan_src + slice * slice_entries;
+  c.plan_dst = pool->plan_dst + slice * slice_entries;
+  c.plan_cnt = pool->plan_cnt + (size_t)slice * pool->cfg.max_batch;
   c.stats = (unsigned long long*)stats;
   c.plan_stride = pool->cfg.max_top_k;
   c.units = pool->cfg.row_bytes / 16;
@@ -206,8 +208,8 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   if (c.row_bytes <= 0 || c.row_bytes % 16 != 0)
     return fail(HISPARSE_EINVAL, "row_bytes %d is not a positive multiple of 16", c.row_bytes);
   if (c.num_layers <= 0) return fail(HISPARSE_EINVAL, "num_layers must be > 0");
-  if (c.page_size < 0 || c.resident_pages < 0 || c.reserved != 0)
-    return fail(HISPARSE_EINVAL, "page_size / resident_pages must be >= 0, reserved must be 0");
+  if (c.page_size < 0 || c.resident_pages < 0 || c.max_steps < 0)
+    return fail(HISPARSE_EINVAL, "page_size / resident_pages / max_steps must be >= 0");
   if (c.resident_pages > 0 && c.page_size == 0)
     return fail(HISPARSE_EINVAL, "resident_pages > 0 needs page_size > 0");
   if (c.max_seq_len <= 0 || c.max_seq_len > INT32_MAX)
@@ -284,8 +286,10 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   }
   memcpy(pool->host_rows, host_pool_rows, (size_t)L * sizeof(int64_t));
 
-  const size_t entries = (size_t)c.max_batch * c.max_top_k;
-  const size_t bytes_src = entries * 8, bytes_dst = entries * 4, bytes_cnt = (size_t)c.max_batch * 4;
+  const size_t slices = c.max_steps > 1 ? (size_t)c.max_steps : 1;  // one plan per verification step
+  const size_t entries = (size_t)c.max_batch * c.max_top_k * slices;
+  const size_t bytes_src = entries * 8, bytes_dst = entries * 4;
+  const size_t bytes_cnt = (size_t)c.max_batch * slices * 4;
   const size_t bytes_tab = (size_t)L * 8;
   unsigned char* ws = nullptr;
   const size_t total = align16(bytes_src) + align16(bytes_dst) + align16(bytes_cnt) +
@@ -391,6 +395,66 @@ int hisparse_resolve(hisparse_pool* pool, void* stream, int32_t batch, int32_t t
                    device_buffer_locs, stats, fuse ? pool->cfg.num_layers : 0);
   if (rc != HISPARSE_OK || fuse) return rc == HISPARSE_OK ? ok() : rc;
   rc = launch_copy(pool, (hipStream_t)stream, batch, 0, pool->cfg.num_layers, stats);
+  return rc == HISPARSE_OK ? ok() : rc;
+}
+
+int hisparse_resolve_steps(hisparse_pool* pool, void* stream, int32_t steps, int32_t batch,
+                           int32_t top_k, const int32_t* req_idx, const int32_t* top_k_tokens,
+                           const int32_t* seq_lens, const int64_t* host_cache_locs,
+                           const int32_t* resident_block_table, int32_t* slot_tokens,
+                           int32_t* lru_slots, int32_t* lru_clock, int32_t* device_buffer_locs,
+                           uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  const int32_t max_steps = pool->cfg.max_steps > 1 ? pool->cfg.max_steps : 1;
+  if (steps < 0 || steps > max_steps)
+    return fail(HISPARSE_EINVAL, "steps %d outside [0, max_steps=%d]", steps, max_steps);
+  if ((int64_t)steps * top_k > pool->cfg.slots)
+    return fail(HISPARSE_EINVAL,
+                "steps %d x top_k %d exceed slots %d: a later step could evict a row an earlier "
+                "step of the same call still needs",
+                steps, top_k, pool->cfg.slots);
+  for (int32_t q = 0; q < steps; ++q) {
+    const size_t off = (size_t)q * batch * top_k;
+    const int32_t* tk = top_k_tokens ? top_k_tokens + off : nullptr;
+    int32_t* out = device_buffer_locs ? device_buffer_locs + off : nullptr;
+    const int32_t* sl = seq_lens ? seq_lens + (size_t)q * batch : nullptr;
+    int rc = check_resolve_args(pool, batch, top_k, req_idx, tk, sl,
+                                host_cache_locs, resident_block_table, slot_tokens, lru_slots,
+                                lru_clock, out, stats);
+    if (rc != HISPARSE_OK) return rc;
+    if (batch == 0) return ok();
+    if (q == 0 && (rc = check_device(pool)) != HISPARSE_OK) return rc;
+    // Each step is planned into its own slice (replayable); steps run in
+    // stream order, so step q sees the stamps of steps < q.
+    const bool fuse = batch >= kFuseMinBatch && pool->cfg.num_layers <= kMaxFusedLayers;
+    rc = launch_plan(pool, (hipStream_t)stream, batch, top_k, req_idx, tk, sl,
+                     host_cache_locs, resident_block_table,
+                     slot_tokens, lru_slots, lru_clock, out, stats,
+                     fuse ? pool->cfg.num_layers : 0, q);
+    if (rc != HISPARSE_OK) return rc;
+    if (!fuse && (rc = launch_copy(pool, (hipStream_t)stream, batch, 0, pool->cfg.num_layers,
+                                   stats, q)) != HISPARSE_OK)
+      return rc;
+  }
+  return ok();
+}
+
+int hisparse_gather_copy_step(hisparse_pool* pool, void* stream, int32_t step, int32_t batch,
+                              int32_t layer_begin, int32_t layer_end, uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  const int32_t max_steps = pool->cfg.max_steps > 1 ? pool->cfg.max_steps : 1;
+  if (step < 0 || step >= max_steps)
+    return fail(HISPARSE_EINVAL, "step %d outside [0, max_steps=%d)", step, max_steps);
+  if (batch < 0 || batch > pool->cfg.max_batch)
+    return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
+  if (layer_begin < 0 || layer_end > pool->cfg.num_layers || layer_begin > layer_end)
+    return fail(HISPARSE_EINVAL, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
+                pool->cfg.num_layers);
+  if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
+  if (batch == 0 || layer_begin == layer_end) return ok();
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  rc = launch_copy(pool, (hipStream_t)stream, batch, layer_begin, layer_end, stats, step);
   return rc == HISPARSE_OK ? ok() : rc;
 }
 

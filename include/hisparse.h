@@ -83,7 +83,9 @@ typedef struct {
                              fp8 sparse-MLA row)                                 */
   int32_t num_layers;     /* L >= 1 layers that share one index and one plan    */
   int32_t page_size;      /* P: tokens per resident page; 0 = no resident tier  */
-  int32_t reserved;       /* must be 0                                           */
+  int32_t max_steps;      /* verification steps per hisparse_resolve_steps call
+                             (speculative decoding); 0 or 1 = one.  The miss
+                             plan workspace holds this many slices.             */
   int64_t resident_pages; /* resident pages in each device pool (0 if P == 0)   */
   int64_t max_seq_len;    /* row stride, in tokens, of host_cache_locs and
                              (divided by P, rounded up) of the block table      */
@@ -236,6 +238,36 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream,
                                int32_t layer, const void* q_bf16,
                                const int32_t* device_buffer_locs,
                                float softmax_scale, void* out_bf16);
+
+/*
+ * hisparse_resolve_steps -- the verification steps of speculative decoding
+ * (multi-token prediction): `steps` resolver steps in order, each exactly
+ * hisparse_resolve on its own slice of the arguments, with step q planned
+ * into plan slice q of the workspace (replayable with
+ * hisparse_gather_copy_step) and all steps sharing the requests' hot state
+ * ("vLLM Hybrid HiSparse 源码实现分析" section 7.4; the architecture page's
+ * note on speculative decoding).
+ *   top_k_tokens        [steps][batch][top_k]
+ *   seq_lens            [steps][batch]
+ *   device_buffer_locs  [steps][batch][top_k] (out)
+ * Requires steps <= max(1, config.max_steps) and steps * top_k <= slots:
+ * then every victim of step q is older than this call, so no step evicts a
+ * row that an earlier step of the same call returned (the page's hot
+ * region of (query length + 1) * top_k rows meets this with one top_k to
+ * spare).  Errors: as hisparse_resolve, and EINVAL for the two bounds.
+ */
+int hisparse_resolve_steps(hisparse_pool* pool, void* stream, int32_t steps, int32_t batch,
+                           int32_t top_k, const int32_t* req_idx, const int32_t* top_k_tokens,
+                           const int32_t* seq_lens, const int64_t* host_cache_locs,
+                           const int32_t* resident_block_table, int32_t* slot_tokens,
+                           int32_t* lru_slots, int32_t* lru_clock, int32_t* device_buffer_locs,
+                           uint64_t* stats);
+
+/* hisparse_gather_copy_step -- hisparse_gather_copy of plan slice `step`
+ * (0 <= step < max(1, max_steps)), e.g. for the follower layers of one
+ * verification step.  Errors: EINVAL, EHIP. */
+int hisparse_gather_copy_step(hisparse_pool* pool, void* stream, int32_t step, int32_t batch,
+                              int32_t layer_begin, int32_t layer_end, uint64_t* stats);
 
 /*
  * hisparse_mirror_rows -- the row mirror (eager backup): copy device rows

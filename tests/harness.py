@@ -31,7 +31,8 @@ def make_host_pools(w, kind="uniform", seed_base=100, gen_device="cuda"):
 class Pair:
     """The GPU side and the oracle side of one workload."""
 
-    def __init__(self, w, host_bufs, with_oracle=True, max_batch=None, mode="resolve"):
+    def __init__(self, w, host_bufs, with_oracle=True, max_batch=None, mode="resolve",
+                 max_steps=1):
         """mode "resolve": the single-call entry point (which copies inside the
         plan kernel at batch >= 8 with <= 8 layers); "split": the plan entry
         point followed by the separate copy entry point."""
@@ -47,7 +48,7 @@ class Pair:
         cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k,
                             max_batch=max_batch or w.B, row_bytes=w.row_bytes,
                             num_layers=w.L, page_size=w.P, resident_pages=w.resident_pages,
-                            max_seq_len=w.max_seq_len)
+                            max_seq_len=w.max_seq_len, max_steps=max_steps)
         self.pool = hs.hisparse_init_pool(cfg, host_bufs, [w.host_pool_rows] * w.L,
                                           self.dev_pools, w.dev_pool_rows)
         st, lru, clk, dst, src = admission(w)
@@ -79,6 +80,17 @@ class Pair:
         for l in range(self.w.L):
             rows = self.host_t[l][torch.from_numpy(src)].cuda()
             self.dev_pools[l].index_copy_(0, d, rows)
+
+    def writes_of(self, step):
+        """The forward pass's fast-path row writes before `step`."""
+        return decode_writes(self.w, step)
+
+    def pre_step_writes(self, step):
+        """Apply those writes to the GPU pools only (the oracle applies them in
+        oracle_step)."""
+        dst, src = decode_writes(self.w, step)
+        self._copy_rows(dst, src)
+        return dst, src
 
     def gpu_step(self, step, stream=None):
         w = self.w
