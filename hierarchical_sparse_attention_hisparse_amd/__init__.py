@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     HostBuffer,
     PoolConfig,
     STAT_NAMES,
+    hisparse_decode_layers_overlapped,
     hisparse_destroy_pool,
     hisparse_gather_copy,
     hisparse_gather_copy_step,

@@ -29,6 +29,7 @@ struct hisparse_pool {
   uint4* zero_row;              // row_bytes of zeros (source of out-of-range host rows)
   void* dec_ws;                 // decode split partials, grown on demand
   size_t dec_ws_bytes;
+  hipEvent_t* layer_ready;      // [L + 1] for the overlapped decode, created on first use
   // host copies
   unsigned char** dev_ptrs;     // [L]
   unsigned char** host_ptrs;    // [L] device-mapped host pool pointers
@@ -334,6 +335,10 @@ void hisparse_destroy_pool(hisparse_pool* pool) {
   if (!pool) return;
   if (pool->plan_src) (void)hipFree(pool->plan_src);
   if (pool->dec_ws) (void)hipFree(pool->dec_ws);
+  if (pool->layer_ready) {
+    for (int l = 0; l <= pool->cfg.num_layers; ++l) (void)hipEventDestroy(pool->layer_ready[l]);
+    free(pool->layer_ready);
+  }
   free(pool->dev_ptrs);
   free(pool->host_ptrs);
   free(pool->host_rows);
@@ -547,7 +552,7 @@ int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t cou
   return ok();
 }
 
-int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,
+static int decode_one(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,
                                int32_t top_k, int32_t layer, const void* q_bf16,
                                const int32_t* device_buffer_locs, float softmax_scale,
                                void* out_bf16) {
@@ -606,6 +611,61 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch,
   d.out = (uint16_t*)out_bf16;
   hipError_t e = launch_sparse_mla_decode(d, batch, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sparse-MLA decode kernel launch");
+  return ok();
+}
+
+int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,
+                               int32_t top_k, int32_t layer, const void* q_bf16,
+                               const int32_t* device_buffer_locs, float softmax_scale,
+                               void* out_bf16) {
+  return decode_one(pool, stream, batch, heads, top_k, layer, q_bf16, device_buffer_locs,
+                    softmax_scale, out_bf16);
+}
+
+int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* compute_stream,
+                                      void* copy_stream, int32_t batch, int32_t heads,
+                                      int32_t top_k, const void* const* q_bf16,
+                                      const int32_t* device_buffer_locs, float softmax_scale,
+                                      void* const* out_bf16, uint64_t* stats) {
+  if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
+  if (!q_bf16 || !out_bf16) return fail(HISPARSE_EINVAL, "q_bf16 and out_bf16 must not be NULL");
+  if (compute_stream == copy_stream)
+    return fail(HISPARSE_EINVAL, "the copy stream must differ from the compute stream");
+  if (batch < 0 || batch > pool->cfg.max_batch)
+    return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
+  if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
+  if (batch == 0) return ok();
+  int rc = check_device(pool);
+  if (rc != HISPARSE_OK) return rc;
+  const int L = pool->cfg.num_layers;
+  if (!pool->layer_ready) {
+    hipEvent_t* ev = (hipEvent_t*)calloc((size_t)L + 1, sizeof(hipEvent_t));
+    if (!ev) return fail(HISPARSE_ENOMEM, "host allocation failed");
+    for (int l = 0; l <= L; ++l) {
+      hipError_t e = hipEventCreateWithFlags(&ev[l], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        for (int j = 0; j < l; ++j) (void)hipEventDestroy(ev[j]);
+        free(ev);
+        return hip_fail(e, "hipEventCreateWithFlags");
+      }
+    }
+    pool->layer_ready = ev;
+  }
+  hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
+  // the plan (enqueued on the compute stream before this call) comes first
+  hipError_t e = hipEventRecord(pool->layer_ready[L], cs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ps, pool->layer_ready[L], 0);
+  if (e != hipSuccess) return hip_fail(e, "plan event");
+  for (int l = 0; l < L; ++l) {
+    rc = launch_copy(pool, ps, batch, l, l + 1, stats);
+    if (rc != HISPARSE_OK) return rc;
+    e = hipEventRecord(pool->layer_ready[l], ps);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, pool->layer_ready[l], 0);
+    if (e != hipSuccess) return hip_fail(e, "layer event");
+    rc = decode_one(pool, compute_stream, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
+                    softmax_scale, out_bf16[l]);
+    if (rc != HISPARSE_OK) return rc;
+  }
   return ok();
 }
 

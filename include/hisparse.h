@@ -323,6 +323,27 @@ int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t cou
                                   const int64_t* rows_sorted, const int64_t* host_cache_locs,
                                   int32_t* slot_tokens, int32_t* lru_slots);
 
+/*
+ * hisparse_decode_layers_overlapped -- the miss copy and the decode of every
+ * layer, pipelined over two streams: after a plan (hisparse_resolve_plan or
+ * the plan of hisparse_resolve_steps' slice 0) enqueued on compute_stream,
+ * layer l's copy runs on copy_stream and is followed by its own ready event;
+ * compute_stream waits for that event and runs layer l's decode, so the copy
+ * of layer l+1 overlaps the attention of layer l.  This is the layer-group
+ * pipelining of "vLLM Hybrid HiSparse 源码实现分析" section 6 (each group is
+ * submitted when ready and synchronised by its last layer's event) applied
+ * to the swap-in side.  Results are those of hisparse_gather_copy of all
+ * layers followed by hisparse_sparse_mla_decode of each layer l with
+ * q_bf16[l] and out_bf16[l] (host arrays of L device pointers).  When it
+ * returns, compute_stream is ordered after every copy.  The two streams must
+ * differ; both keep default priority.  Errors: as those two calls.
+ */
+int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* compute_stream,
+                                      void* copy_stream, int32_t batch, int32_t heads,
+                                      int32_t top_k, const void* const* q_bf16,
+                                      const int32_t* device_buffer_locs, float softmax_scale,
+                                      void* const* out_bf16, uint64_t* stats);
+
 /* Free the pool's workspace and the pool.  NULL is a no-op.  The caller must
  * make sure no work that uses the pool is still queued. */
 void hisparse_destroy_pool(hisparse_pool* pool);
