@@ -89,7 +89,8 @@ def setup_gpu(w, torch, hs, host_buf):
     pools = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)]
     cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
                         row_bytes=w.row_bytes, num_layers=w.L, page_size=w.P,
-                        resident_pages=w.resident_pages, max_seq_len=w.max_seq_len)
+                        resident_pages=w.resident_pages, max_seq_len=w.max_seq_len,
+                        max_steps=2)
     pool = hs.hisparse_init_pool(cfg, [host_buf], [w.host_pool_rows], pools, w.dev_pool_rows)
     st, lru, clk, dst, src = admission(w)
     # the forward pass's KV writes of fast-path requests for every step, ahead
@@ -117,6 +118,187 @@ def reset_state(g):
     g["lru"].copy_(g["lru"].new_tensor(g["lru0"]))
     g["clk"].copy_(g["clk"].new_tensor(g["clk0"]))
     g["stats"].zero_()
+
+
+def measure_d2h_peak(torch, nbytes=1 << 30, reps=10):
+    d = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    best = 1e30
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        h.copy_(d, non_blocking=True)
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e))
+    del h, d
+    return nbytes / (best * 1e-3) / 1e9
+
+
+def time_calls(torch, stream, fn, reps):
+    """Average ms of `reps` back-to-back calls on `stream` (after one more)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, warmup, steps):
+    """The rows after the resolver: row mirror, invalidation, the verification
+    steps of speculative decoding and the copy/decode overlap over layers.
+    Run after the timed region on the state it left.  The mirror writes into
+    a scratch host pool of its own (a random permutation of its rows), so
+    the workload's host pool is untouched."""
+    from workloads import fill_host_rows_mla, make_queries
+    res = {}
+    dev = torch.device("cuda")
+    st_np = g["st"].cpu().numpy()
+    # ---- row mirror: every occupied hot slot back to its token's host row
+    d_rows, first_d = [], []
+    for b in range(w.B):
+        r = int(w.req_idx[b])
+        if r < 0:
+            continue
+        s_idx = np.nonzero((st_np[r] >= 0) & (st_np[r] < w.max_seq_len))[0]
+        if len(s_idx) == 0:
+            continue
+        d_rows.append(r * w.S + s_idx)
+        first_d.append(d_rows[-1][-1])
+    d_np = np.concatenate(d_rows).astype(np.int32)
+    n_m = len(d_np)
+    scratch = hs.HostBuffer(n_m * ROW_BYTES)
+    cfg_m = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                          row_bytes=w.row_bytes, max_seq_len=w.max_seq_len)
+    pool_m = hs.hisparse_init_pool(cfg_m, [scratch], [n_m], g["pools"], w.dev_pool_rows)
+    perm = np.random.default_rng(11).permutation(n_m).astype(np.int64)
+    d_all = torch.from_numpy(d_np).to(dev)
+    h_all = torch.from_numpy(perm).to(dev)
+    d_one = torch.from_numpy(np.array(first_d, np.int32)).to(dev)
+    h_one = torch.from_numpy(perm[:len(first_d)].copy()).to(dev)
+    bulk_ms = time_calls(torch, stream, lambda: hs.hisparse_mirror_rows(pool_m, stream, d_all, h_all), 3)
+    step_ms = time_calls(torch, stream, lambda: hs.hisparse_mirror_rows(pool_m, stream, d_one, h_one), 50)
+    hs.hisparse_destroy_pool(pool_m)
+    scratch.free()
+    d2h = measure_d2h_peak(torch)
+    bulk_gbs = n_m * ROW_BYTES / (bulk_ms * 1e-3) / 1e9
+    res["row_mirror"] = {
+        "kernel": "mirror_rows_kernel (device rows -> pinned host rows)",
+        "bulk_rows": n_m, "bulk_ms": bulk_ms, "bulk_gbs": bulk_gbs,
+        "bound": "host_link", "peak": HOST_LINK_PEAK_GBS, "frac": bulk_gbs / HOST_LINK_PEAK_GBS,
+        "measured_peak_d2h_memcpy": d2h, "frac_of_measured_peak": bulk_gbs / d2h,
+        "per_step_rows": len(d_one), "per_step_us": step_ms * 1e3,
+    }
+    # ---- invalidation on copies of the state
+    rng = np.random.default_rng(3)
+    longs = [int(w.req_idx[b]) for b in range(w.B)
+             if w.req_idx[b] >= 0 and w.seq_lens[-1, b] > w.S]
+    pages = [(longs[i % len(longs)], int(rng.integers(0, 500))) for i in range(64)]
+    rows = np.unique(np.concatenate([w.host_cache_locs[r, 64 * p:64 * p + 64] for r, p in pages]))
+    rows_t = torch.from_numpy(rows.astype(np.int64)).to(dev)
+    st_c, lru_c = g["st"].clone(), g["lru"].clone()
+    inv_ms = time_calls(torch, stream, lambda: hs.hisparse_invalidate_host_rows(
+        g["pool"], stream, rows_t, g["locs"], st_c, lru_c), 20)
+    occupied = int((st_np >= 0).sum())
+    inv_bytes = w.R * w.S * 4 + occupied * 8
+    req_t = torch.from_numpy(w.req_idx.astype(np.int32)).to(dev)
+    hi = torch.from_numpy(w.seq_lens[-1].astype(np.int32)).to(dev)
+    lo = hi - 64
+    tok_ms = time_calls(torch, stream, lambda: hs.hisparse_invalidate_tokens(
+        g["pool"], stream, req_t, lo, hi, st_c, lru_c), 20)
+    res["invalidate"] = {
+        "host_rows_kernel": "invalidate_host_rows_kernel (sorted set in LDS, binary search)",
+        "host_rows": len(rows), "slots_scanned": w.R * w.S, "host_rows_us": inv_ms * 1e3,
+        "host_rows_algorithmic_bytes": inv_bytes,
+        "host_rows_gbs": inv_bytes / (inv_ms * 1e-3) / 1e9, "bound": "hbm", "peak": HBM_PEAK_GBS,
+        "frac": inv_bytes / (inv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "token_ranges": len(req_t), "token_ranges_us": tok_ms * 1e3,
+    }
+    # ---- verification steps of speculative decoding (MTP1: 2 steps, S = 2k)
+    restore(snap)
+    torch.cuda.synchronize()
+    out2 = torch.empty((2, w.B, w.k), dtype=torch.int32, device=dev)
+    calls = steps // 2
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for j in range(calls):
+        i = warmup + 2 * j
+        hs.hisparse_resolve_steps(g["pool"], stream, 2, w.B, w.k, g["req"], g["topk"][i:i + 2],
+                                  g["seq"][i:i + 2], g["locs"], None, g["st"], g["lru"], g["clk"],
+                                  out2, g["stats"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mtp_ms = e0.elapsed_time(e1) / calls
+    mtp_rows = sum(w.valid_entries(warmup + j) for j in range(2 * calls)) / calls
+    res["speculative_steps"] = {
+        "steps_per_call": 2, "calls": calls, "ms_per_call": mtp_ms,
+        "rows_resolved_per_s": mtp_rows / (mtp_ms * 1e-3),
+        "note": "two verification steps per decode step, slots = 2 x top_k",
+    }
+    # ---- copy/decode overlap over 4 layers sharing the index, each with its
+    # own host pool and device pool
+    L = 4
+    extra = []
+    for l in range(1, L):
+        hb = hs.HostBuffer(w.host_pool_rows * ROW_BYTES)
+        fill_host_rows_mla(hb.torch((w.host_pool_rows, ROW_BYTES)), seed=300 + l, gen_device="cuda")
+        extra.append(hb)
+    pools4 = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)
+              for _ in range(L)]
+    cfg4 = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                         row_bytes=w.row_bytes, num_layers=L, max_seq_len=w.max_seq_len)
+    pool4 = hs.hisparse_init_pool(cfg4, [host_buf] + extra, [w.host_pool_rows] * L, pools4,
+                                  w.dev_pool_rows)
+    qs = [make_queries(w.B, DECODE_HEADS, seed=80 + l, device="cuda") for l in range(L)]
+    outs = [torch.empty((w.B, DECODE_HEADS, 512), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    scale = 1.0 / math.sqrt(192.0)
+
+    def run(overlapped, n_steps):
+        g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+        # a warm-up step from the same state, then n_steps timed
+        for j in range(n_steps + 1):
+            if j == 1:
+                torch.cuda.synchronize()
+                ev[0].record(stream)
+            i = warmup + j
+            hs.hisparse_resolve_plan(pool4, stream, w.B, w.k, g["req"], g["topk"][i], g["seq"][i],
+                                     g["locs"], None, g["st"], g["lru"], g["clk"], g["out"], None)
+            if overlapped:
+                hs.hisparse_decode_layers_overlapped(pool4, stream, w.B, DECODE_HEADS, w.k, qs,
+                                                     g["out"], scale, outs)
+            else:
+                hs.hisparse_gather_copy(pool4, stream, w.B, 0, L)
+                for l in range(L):
+                    hs.hisparse_sparse_mla_decode(pool4, stream, w.B, DECODE_HEADS, w.k, l, qs[l],
+                                                  g["out"], scale, outs[l])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n_steps
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n_ovl = min(8, steps - 1)
+    seq_ms = run(False, n_ovl)
+    ovl_ms = run(True, n_ovl)
+    hs.hisparse_destroy_pool(pool4)
+    del pools4
+    for hb in extra:
+        hb.free()
+    res["copy_decode_overlap"] = {
+        "layers": L, "heads": DECODE_HEADS, "steps": n_ovl,
+        "sequential_ms_per_step": seq_ms, "overlapped_ms_per_step": ovl_ms,
+        "speedup": seq_ms / ovl_ms,
+        "note": "plan, then per layer: miss copy and decode on the pool's two streams vs "
+                "the same kernels in order on one stream",
+    }
+    return res
 
 
 def host_cpu_model():
@@ -397,6 +579,9 @@ def main():
     dec_tflops = dec_flop / (dec_ms * 1e-3) / 1e12
     assert torch.isfinite(out.float()).all()
 
+    log("rows after the resolver: mirror, invalidation, verification steps, overlap")
+    nxt = next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, args.warmup, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -478,6 +663,7 @@ def main():
             "sequential_cold_misses": seq_misses,
             "sequential_cold_ms": seq_ms,
         },
+        "next_rows": nxt,
         "cpu_baseline": cpu,
         "consumer_sparse_mla_decode": {
             "kernel": "sparse_mla_decode (128 heads, fp8 latent + bf16 rope rows, bf16 MFMA)",

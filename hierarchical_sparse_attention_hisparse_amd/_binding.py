@@ -94,7 +94,7 @@ def load_library():
     lib.hisparse_invalidate_host_rows.restype = ctypes.c_int
     lib.hisparse_invalidate_host_rows.argtypes = [V, V, I32, V, V, V, V]
     lib.hisparse_decode_layers_overlapped.restype = I
-    lib.hisparse_decode_layers_overlapped.argtypes = [V, V, V, I32, I32, I32, V, V,
+    lib.hisparse_decode_layers_overlapped.argtypes = [V, V, I32, I32, I32, V, V,
                                                       ctypes.c_float, V, V]
     lib.hisparse_sparse_mla_decode.restype = I
     lib.hisparse_sparse_mla_decode.argtypes = [V, V, I32, I32, I32, I32, V, V,
@@ -362,11 +362,11 @@ def hisparse_sparse_mla_decode(pool, stream, batch, heads, top_k, layer, q_bf16,
               "hisparse_sparse_mla_decode")
 
 
-def hisparse_decode_layers_overlapped(pool, compute_stream, copy_stream, batch, heads, top_k,
-                                      q_per_layer, device_buffer_locs, softmax_scale,
-                                      out_per_layer, stats=None):
-    """Per-layer miss copy on ``copy_stream`` pipelined with per-layer decode on
-    ``compute_stream`` (after a plan on ``compute_stream``)."""
+def hisparse_decode_layers_overlapped(pool, stream, batch, heads, top_k, q_per_layer,
+                                      device_buffer_locs, softmax_scale, out_per_layer,
+                                      stats=None):
+    """Per-layer miss copy pipelined with per-layer decode on the pool's two
+    streams, after a plan on ``stream``; ``stream`` waits for both."""
     import torch
     L = pool.cfg.num_layers
     if len(q_per_layer) != L or len(out_per_layer) != L:
@@ -378,6 +378,6 @@ def hisparse_decode_layers_overlapped(pool, compute_stream, copy_stream, batch, 
     lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs")
     sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
     _check_rc(load_library().hisparse_decode_layers_overlapped(
-        pool.handle, _stream_handle(compute_stream), _stream_handle(copy_stream), batch, heads,
-        top_k, ctypes.cast(qs, ctypes.c_void_p), lp, ctypes.c_float(softmax_scale),
+        pool.handle, _stream_handle(stream), batch, heads, top_k, ctypes.cast(qs, ctypes.c_void_p), lp, ctypes.c_float(softmax_scale),
         ctypes.cast(outs, ctypes.c_void_p), sp), "hisparse_decode_layers_overlapped")
+

@@ -29,7 +29,10 @@ struct hisparse_pool {
   uint4* zero_row;              // row_bytes of zeros (source of out-of-range host rows)
   void* dec_ws;                 // decode split partials, grown on demand
   size_t dec_ws_bytes;
-  hipEvent_t* layer_ready;      // [L + 1] for the overlapped decode, created on first use
+  // overlapped decode, created on first use: per-layer ready events plus
+  // entry / exit events, and two streams
+  hipEvent_t* layer_ready;      // [L + 3]
+  hipStream_t ovl_copy, ovl_compute;
   // host copies
   unsigned char** dev_ptrs;     // [L]
   unsigned char** host_ptrs;    // [L] device-mapped host pool pointers
@@ -336,9 +339,11 @@ void hisparse_destroy_pool(hisparse_pool* pool) {
   if (pool->plan_src) (void)hipFree(pool->plan_src);
   if (pool->dec_ws) (void)hipFree(pool->dec_ws);
   if (pool->layer_ready) {
-    for (int l = 0; l <= pool->cfg.num_layers; ++l) (void)hipEventDestroy(pool->layer_ready[l]);
+    for (int l = 0; l < pool->cfg.num_layers + 3; ++l) (void)hipEventDestroy(pool->layer_ready[l]);
     free(pool->layer_ready);
   }
+  if (pool->ovl_copy) (void)hipStreamDestroy(pool->ovl_copy);
+  if (pool->ovl_compute) (void)hipStreamDestroy(pool->ovl_compute);
   free(pool->dev_ptrs);
   free(pool->host_ptrs);
   free(pool->host_rows);
@@ -622,15 +627,21 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch,
                     softmax_scale, out_bf16);
 }
 
-int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* compute_stream,
-                                      void* copy_stream, int32_t batch, int32_t heads,
-                                      int32_t top_k, const void* const* q_bf16,
+// Streams of the overlapped decode: two plain non-blocking streams of the
+// pool, default priority.
+static int make_overlap_streams(hisparse_pool* pool) {
+  hipError_t e = hipStreamCreateWithFlags(&pool->ovl_copy, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&pool->ovl_compute, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+  return HISPARSE_OK;
+}
+
+int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t batch,
+                                      int32_t heads, int32_t top_k, const void* const* q_bf16,
                                       const int32_t* device_buffer_locs, float softmax_scale,
                                       void* const* out_bf16, uint64_t* stats) {
   if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
   if (!q_bf16 || !out_bf16) return fail(HISPARSE_EINVAL, "q_bf16 and out_bf16 must not be NULL");
-  if (compute_stream == copy_stream)
-    return fail(HISPARSE_EINVAL, "the copy stream must differ from the compute stream");
   if (batch < 0 || batch > pool->cfg.max_batch)
     return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
   if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
@@ -638,10 +649,11 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* compute_stream,
   int rc = check_device(pool);
   if (rc != HISPARSE_OK) return rc;
   const int L = pool->cfg.num_layers;
+  if (!pool->ovl_copy && (rc = make_overlap_streams(pool)) != HISPARSE_OK) return rc;
   if (!pool->layer_ready) {
-    hipEvent_t* ev = (hipEvent_t*)calloc((size_t)L + 1, sizeof(hipEvent_t));
+    hipEvent_t* ev = (hipEvent_t*)calloc((size_t)L + 3, sizeof(hipEvent_t));
     if (!ev) return fail(HISPARSE_ENOMEM, "host allocation failed");
-    for (int l = 0; l <= L; ++l) {
+    for (int l = 0; l < L + 3; ++l) {
       hipError_t e = hipEventCreateWithFlags(&ev[l], hipEventDisableTiming);
       if (e != hipSuccess) {
         for (int j = 0; j < l; ++j) (void)hipEventDestroy(ev[j]);
@@ -651,21 +663,27 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* compute_stream,
     }
     pool->layer_ready = ev;
   }
-  hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
-  // the plan (enqueued on the compute stream before this call) comes first
-  hipError_t e = hipEventRecord(pool->layer_ready[L], cs);
-  if (e == hipSuccess) e = hipStreamWaitEvent(ps, pool->layer_ready[L], 0);
-  if (e != hipSuccess) return hip_fail(e, "plan event");
+  hipStream_t cs = pool->ovl_compute, ps = pool->ovl_copy, us = (hipStream_t)stream;
+  hipEvent_t* ev = pool->layer_ready;
+  // both streams start after the caller's work so far (the plan included)
+  hipError_t e = hipEventRecord(ev[L], us);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ps, ev[L], 0);
+  if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[L], 0);
+  if (e != hipSuccess) return hip_fail(e, "entry event");
   for (int l = 0; l < L; ++l) {
     rc = launch_copy(pool, ps, batch, l, l + 1, stats);
     if (rc != HISPARSE_OK) return rc;
-    e = hipEventRecord(pool->layer_ready[l], ps);
-    if (e == hipSuccess) e = hipStreamWaitEvent(cs, pool->layer_ready[l], 0);
+    e = hipEventRecord(ev[l], ps);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[l], 0);
     if (e != hipSuccess) return hip_fail(e, "layer event");
-    rc = decode_one(pool, compute_stream, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
+    rc = decode_one(pool, cs, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
                     softmax_scale, out_bf16[l]);
     if (rc != HISPARSE_OK) return rc;
   }
+  // the caller's stream continues after the last decode (which follows every copy)
+  e = hipEventRecord(ev[L + 1], cs);
+  if (e == hipSuccess) e = hipStreamWaitEvent(us, ev[L + 1], 0);
+  if (e != hipSuccess) return hip_fail(e, "exit event");
   return ok();
 }
 

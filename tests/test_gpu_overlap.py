@@ -26,7 +26,6 @@ def test_overlapped_layers_match_sequential(B):
     bufs = make_host_pools(w, kind="mla")
     seq = Pair(w, bufs, with_oracle=False)
     ovl = Pair(w, bufs)
-    copy_stream = torch.cuda.Stream()
     try:
         qs = [make_queries(w.B, H, seed=10 + l, device="cuda") for l in range(L)]
         for step in range(w.steps):
@@ -41,8 +40,8 @@ def test_overlapped_layers_match_sequential(B):
             for l in range(L):
                 hs.hisparse_sparse_mla_decode(seq.pool, None, w.B, H, w.k, l, qs[l], seq.out, SCALE,
                                               outs_s[l])
-            hs.hisparse_decode_layers_overlapped(ovl.pool, None, copy_stream, w.B, H, w.k, qs,
-                                                 ovl.out, SCALE, outs_o, ovl.stats)
+            hs.hisparse_decode_layers_overlapped(ovl.pool, None, w.B, H, w.k, qs, ovl.out, SCALE,
+                                                 outs_o, ovl.stats)
             torch.cuda.synchronize()
             assert torch.equal(seq.out, ovl.out)
             for l in range(L):
