@@ -151,6 +151,105 @@ def time_calls(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def mixed_residency_legs(hs, torch, stream, reuses=(0.5, 0.99, 1.0)):
+    """Mixed residency: 128 requests of 131072 tokens whose last 16384 tokens
+    sit in resident pages of 64 (resolved in place), 4096 hot slots,
+    top-2048, 32 steps from cold per reuse fraction.  50 % reuse is the
+    miss-heavy case, 99 % the hit-heavy one, 100 % a diagnostic with no miss
+    after step 0.  Per fraction: step 0 (cold) timed alone; steps 1..31 timed
+    through hisparse_resolve (one launch per step at this batch); then the
+    same steps replayed from the state after step 0 through the plan-only
+    entry point, back to back, for the hit path against HBM."""
+    from workloads import config3_mixed_residency, admission, fill_host_rows_uniform
+    dev = torch.device("cuda")
+    w = config3_mixed_residency(reuses[0])
+    host = hs.HostBuffer(w.host_pool_rows * ROW_BYTES)
+    host_t = host.torch((w.host_pool_rows, ROW_BYTES))
+    fill_host_rows_uniform(host_t, seed=3, gen_device="cuda")
+    pools = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)]
+    cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                        row_bytes=w.row_bytes, page_size=w.P, resident_pages=w.resident_pages,
+                        max_seq_len=w.max_seq_len)
+    pool = hs.hisparse_init_pool(cfg, [host], [w.host_pool_rows], pools, w.dev_pool_rows)
+    st0, lru0, clk0, dst, src = admission(w)
+    # resident pages hold their tokens' host rows (chunked host-side gather)
+    for a in range(0, len(dst), 1 << 18):
+        d = torch.from_numpy(dst[a:a + (1 << 18)]).to(dev)
+        pools[0].index_copy_(0, d, host_t[torch.from_numpy(src[a:a + (1 << 18)])].to(dev))
+    locs = torch.from_numpy(w.host_cache_locs).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    req = torch.from_numpy(w.req_idx).to(dev)
+    out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    st, lru, clk = (torch.from_numpy(x).to(dev) for x in (st0, lru0, clk0))
+    stats = torch.zeros(5, dtype=torch.int64, device=dev)
+    res = {}
+    for f in reuses:
+        if f != reuses[0]:
+            w = config3_mixed_residency(f)
+        topk = torch.from_numpy(w.top_k).to(dev)
+        seq = torch.from_numpy(w.seq_lens).to(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        st.copy_(torch.from_numpy(st0)); lru.copy_(torch.from_numpy(lru0))
+        clk.copy_(torch.from_numpy(clk0)); stats.zero_()
+
+        def resolve(i, plan_only=False, with_stats=True):
+            fn = hs.hisparse_resolve_plan if plan_only else hs.hisparse_resolve
+            fn(pool, stream, w.B, w.k, req, topk[i], seq[i], locs, bt, st, lru, clk, out,
+               stats if with_stats else None)
+
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        resolve(0)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        s0 = stats.cpu().numpy().astype(np.int64)
+        snap = (st.clone(), lru.clone(), clk.clone())
+        ev[2].record(stream)
+        for i in range(1, w.steps):
+            resolve(i)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        s1 = stats.cpu().numpy().astype(np.int64)
+        st.copy_(snap[0]); lru.copy_(snap[1]); clk.copy_(snap[2])
+        torch.cuda.synchronize()
+        ev[4].record(stream)
+        for i in range(1, w.steps):
+            resolve(i, plan_only=True, with_stats=False)
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        n = w.steps - 1
+        cold_ms = ev[0].elapsed_time(ev[1])
+        step_ms = ev[2].elapsed_time(ev[3]) / n
+        plan_ms = ev[4].elapsed_time(ev[5]) / n
+        hits, misses, resident, fast, trips = [int(x) for x in (s1 - s0)]
+        valid = hits + misses + resident + fast
+        # per step: top-k read + row IDs written (8k) and slot map + stamps
+        # read (8S) per row, one block-table read per valid entry, a stamp per
+        # touched slot, host location + map write per miss, 16 B per row
+        plan_bytes = (w.B * (8 * w.k + 8 * w.S) + w.B * 16
+                      + (4 * valid + 4 * (hits + misses) + 12 * misses) / n)
+        miss_bytes = misses * ROW_BYTES / n
+        res["reuse_%g" % f] = {
+            "cold_step0_ms": cold_ms, "cold_step0_misses": int(s0[1]),
+            "cold_step0_copy_gbs": int(s0[1]) * ROW_BYTES / (cold_ms * 1e-3) / 1e9,
+            "step_ms": step_ms, "rows_resolved_per_s": valid / n / (step_ms * 1e-3),
+            "hits": hits, "misses": misses, "resident_hits": resident, "tripwires": trips,
+            "miss_copy_gbs": miss_bytes / (step_ms * 1e-3) / 1e9,
+            "plan_only_us": plan_ms * 1e3, "plan_algorithmic_bytes": plan_bytes,
+            "plan_hbm_gbs": plan_bytes / (plan_ms * 1e-3) / 1e9,
+            "plan_hbm_frac": plan_bytes / (plan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        log("mixed residency f=%g: step %.3f ms, plan %.1f us, misses/step %.0f"
+            % (f, step_ms, plan_ms * 1e3, misses / n))
+    hs.hisparse_destroy_pool(pool)
+    del pools
+    host.free()
+    res["workload"] = ("128 requests x 131072 tokens, last 16384 resident (pages of 64), "
+                       "4096 slots, top-2048, 32 steps from cold per reuse fraction; "
+                       "steps 1..31 timed")
+    return res
+
+
 def next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, warmup, steps):
     """The rows after the resolver: row mirror, invalidation, the verification
     steps of speculative decoding and the copy/decode overlap over layers.
@@ -358,6 +457,8 @@ def main():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed-residency", action="store_true",
+                    help="skip the mixed-residency legs (11 GB pinned host pool)")
     ap.add_argument("--cold-reps", type=int, default=10)
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run the warm-up (split entry points), the timed steps "
@@ -582,6 +683,11 @@ def main():
     log("rows after the resolver: mirror, invalidation, verification steps, overlap")
     nxt = next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, args.warmup, args.steps)
 
+    mixed = None
+    if not args.no_mixed_residency:
+        log("mixed residency (128 x 131072 tokens, resident tail) at 50 / 99 / 100 % reuse")
+        mixed = mixed_residency_legs(hs, torch, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -664,6 +770,7 @@ def main():
             "sequential_cold_ms": seq_ms,
         },
         "next_rows": nxt,
+        "mixed_residency": mixed,
         "cpu_baseline": cpu,
         "consumer_sparse_mla_decode": {
             "kernel": "sparse_mla_decode (128 heads, fp8 latent + bf16 rope rows, bf16 MFMA)",

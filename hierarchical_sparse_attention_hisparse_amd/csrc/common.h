@@ -69,6 +69,14 @@ struct ResolveLds {
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
+// Workgroup barrier that orders LDS only: it waits for this wavefront's LDS
+// operations, not for its global loads and stores (__syncthreads also drains
+// the vector-memory counter, so every barrier after a global store or ahead
+// of the first use of a global load would wait for that round trip).  Use it
+// only where no thread reads, after the barrier, global memory that another
+// thread wrote before it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Layout for one table size (cells per top-k entry = factor).
 __host__ __device__ inline ResolveLds resolve_lds_layout_f(int S, int k, int factor) {
   ResolveLds L;

@@ -98,7 +98,6 @@ struct RawPart {
 // __syncthreads() would also wait for those loads, one memory latency per
 // barrier.  The memory clobber keeps the compiler from moving LDS accesses
 // across it.
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Location of top-k entry `kk` of this row, at a clamped (in-range) index.
 __device__ inline int loc_at(const DecodeParams& p, const int32_t* locb, int kk) {

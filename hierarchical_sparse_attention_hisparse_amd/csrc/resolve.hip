@@ -31,11 +31,6 @@
 #include "common.h"
 #include "kernels.h"
 
-// Wavefront reductions of the ROCm device library (DPP based).
-extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_min_u64(
-    unsigned long long);
-extern "C" __device__ __attribute__((const)) int __ockl_wfred_add_i32(int);
-
 namespace hisparse {
 
 namespace {
@@ -48,6 +43,50 @@ typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memo
 __device__ inline int lane_prefix(uint64_t m) {  // popcount of m below this lane
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// One DPP step of a wavefront minimum: lanes whose source is outside the
+// pattern (or whose row is masked off) see the identity ~0.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_min_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFF, (int)v, CTRL, ROWS, 0xF, false);
+  return o < v ? o : v;
+}
+
+// Minimum of a 32-bit value over the 64 lanes, wave-uniform: prefix minima
+// within each row of 16 (row_shr 1, 2, 4, 8), then row 0 into row 1 and
+// row 2 into row 3 (row_bcast:15), then rows 0-1 into rows 2-3
+// (row_bcast:31); lane 63 holds the result.
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  v = dpp_min_step<0x111, 0xF>(v);
+  v = dpp_min_step<0x112, 0xF>(v);
+  v = dpp_min_step<0x114, 0xF>(v);
+  v = dpp_min_step<0x118, 0xF>(v);
+  v = dpp_min_step<0x142, 0xA>(v);
+  v = dpp_min_step<0x143, 0xC>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Minimum of victim keys (occupied << 32 | biased stamp, or ~0) over the
+// wavefront: the occupied bit by ballot, then the stamps of the lanes at
+// that bit by a 32-bit minimum.
+__device__ inline uint64_t wave_min_key(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32);  // 0 empty, 1 occupied, ~0 none
+  const bool any_empty = __ballot(hi == 0) != 0;
+  const bool any_occ = __ballot(hi == 1) != 0;
+  if (!any_empty && !any_occ) return ~0ull;
+  const uint32_t want = any_empty ? 0u : 1u;
+  const uint32_t m = wave_min_u32(hi == want ? (uint32_t)v : 0xFFFFFFFFu);
+  return ((uint64_t)want << 32) | m;
+}
+
+// Sum over the wavefront of small per-lane counts (< 2^BITS), by ballots.
+template <int BITS>
+__device__ inline int wave_sum_small(int v) {
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < BITS; ++q) sum += __popcll(__ballot((v >> q) & 1)) << q;
+  return sum;
 }
 
 // Block-wide exclusive prefix sum of small per-thread counts (< 2^BITS) in
@@ -64,7 +103,7 @@ __device__ inline int block_exscan_small(int c, int* buf, int* total) {
     wt += __popcll(m) << q;
   }
   if (lane == 0) buf[wid] = wt;
-  __syncthreads();
+  lds_barrier();
   int base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kResolveWaves; ++w) {
@@ -76,12 +115,13 @@ __device__ inline int block_exscan_small(int c, int* buf, int* total) {
   return base + pre;
 }
 
-// Block-wide minimum with one barrier; `buf` holds 16 u64 for this call site.
-__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* buf) {
+// Block-wide minimum of victim keys with one barrier; `buf` holds 16 u64 for
+// this call site.
+__device__ inline uint64_t block_min_key(uint64_t v, uint64_t* buf) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const uint64_t wm = __ockl_wfred_min_u64(v);
+  const uint64_t wm = wave_min_key(v);
   if (lane == 0) buf[wid] = wm;
-  __syncthreads();
+  lds_barrier();
   uint64_t m = buf[0];
 #pragma unroll
   for (int w = 1; w < kResolveWaves; ++w) {
@@ -189,6 +229,19 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     lr[j] = lru[s];
   }
 
+  // Block-table entries of this thread's positions, at in-range indices,
+  // issued with the slot-state loads so that both round trips overlap.
+  int pgs[KPT];
+  if (p.bt != nullptr) {
+    const int32_t* btr = p.bt + (int64_t)r * p.max_pages;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int t = tr[j];
+      const bool v = t >= 0 && (int64_t)t < n;
+      pgs[j] = btr[v ? t / p.P : 0];
+    }
+  }
+
   uint64_t* H = (uint64_t*)(smem + L.off_hash);
   int32_t* e_hit = (int32_t*)(smem + L.off_ehit);
   int32_t* e_tok = (int32_t*)(smem + L.off_etok);
@@ -206,21 +259,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
     if (s0 + j < S) s_flag[s0 + j] = 0;
-  __syncthreads();
+  // Barriers below order LDS only: no thread reads global memory that another
+  // thread of the workgroup wrote, so the slot-state loads stay in flight
+  // through step 1 and the row-ID and stamp stores never hold a barrier.
+  lds_barrier();
 
   // Step 1: validity, resident pages, table of pending positions.
   int n_res = 0, n_trip = 0;
   unsigned pend = 0;
-  int pgs[KPT];
-  if (p.bt != nullptr) {  // all block-table loads first, at in-range indices
-    const int32_t* btr = p.bt + (int64_t)r * p.max_pages;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int t = tr[j];
-      const bool v = t >= 0 && (int64_t)t < n;
-      pgs[j] = btr[v ? t / p.P : 0];
-    }
-  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
@@ -249,7 +295,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       h = (h + 1) & (HS - 1);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Step 2: probe the table with every slot's token; the SPT probes of a
   // thread advance together so a wavefront waits for its longest chain once.
@@ -283,7 +329,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     for (int j = 0; j < SPT; ++j)
       if ((live & (1u << j)) && hv[j] != kEmptyCell) atomicMin(&e_hit[(int)(uint32_t)hv[j]], s0 + j);
   }
-  __syncthreads();
+  lds_barrier();
 
   // Step 3: hits and the ordered miss list.
   int n_hit = 0, my_miss = 0;
@@ -304,9 +350,9 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
   {
-    const int a0 = __ockl_wfred_add_i32(n_hit);
-    const int a1 = __ockl_wfred_add_i32(n_res);
-    const int a2 = __ockl_wfred_add_i32(n_trip);
+    const int a0 = wave_sum_small<bits_for(KPT)>(n_hit);
+    const int a1 = wave_sum_small<bits_for(KPT)>(n_res);
+    const int a2 = wave_sum_small<bits_for(KPT)>(n_trip);
     if (lane == 0) {
       scr[kScrStats + wid] = a0;
       scr[kScrStats + 16 + wid] = a1;
@@ -335,7 +381,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     for (int j = 0; j < SPT; ++j)
       if ((cand & (1u << j)) && key[j] < my) my = key[j];
     const uint64_t kmin =
-        block_min_u64(my, (uint64_t*)(scr + kScrRoundMin + 32 * round));
+        block_min_key(my, (uint64_t*)(scr + kScrRoundMin + 32 * round));
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < SPT; ++j) cnt += ((cand & (1u << j)) && key[j] == kmin) ? 1 : 0;
@@ -357,14 +403,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   }
   if (need > 0) {  // many distinct stamps among the victims: sort the rest
     const int N = L.sort_size;
-    __syncthreads();  // the table region is reused for the sort
+    lds_barrier();  // the table region is reused for the sort
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int s = s0 + j;
       if (s < N) s_sort[s] = (cand & (1u << j)) ? ((key[j] << 16) | (uint64_t)s) : ~0ull;
     }
     for (int x = tid + kResolveThreads * SPT; x < N; x += kResolveThreads) s_sort[x] = ~0ull;
-    __syncthreads();
+    lds_barrier();
     for (int size = 2; size <= N; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         for (int x = tid; x < N / 2; x += kResolveThreads) {
@@ -377,7 +423,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
             s_sort[hi] = a;
           }
         }
-        __syncthreads();
+        lds_barrier();
       }
     }
     for (int j = tid; j < need; j += kResolveThreads) {
@@ -385,7 +431,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       victim[vbase + j] = s < S ? s : S - 1;  // always < S: candidates >= misses
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Step 5: the j-th miss takes the j-th victim; emit the compact plan.  The
   // fused copy keeps its own copy of the plan in the (now dead) table region.
@@ -420,7 +466,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // bytes again), so every load is unconditional.
   int copy_trips = 0;
   if (COPY && m_total > 0) {
-    __syncthreads();
+    lds_barrier();
     constexpr int RIF = kCopyRowsInFlight;
     const int U = p.units;
     const int total = m_total * p.copy_layers;
