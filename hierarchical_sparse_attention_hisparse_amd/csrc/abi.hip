@@ -152,7 +152,7 @@ int copy_chunks_for(int batch) {
 }
 
 int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t lb, int32_t le,
-                uint64_t* stats, int32_t slice = 0) {
+                uint64_t* stats, int32_t slice = 0, bool narrow = false) {
   CopyParams c;
   c.host_pools = pool->d_host_ptrs;
   c.dev_pools = pool->d_dev_ptrs;
@@ -166,7 +166,8 @@ int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   c.units = pool->cfg.row_bytes / 16;
   c.chunks = copy_chunks_for(batch);
   c.layer_begin = lb;
-  hipError_t e = launch_gather_copy(c, batch, le - lb, stream);
+  hipError_t e = narrow ? launch_gather_copy_narrow(c, batch, le - lb, kNarrowCopyGroups, stream)
+                        : launch_gather_copy(c, batch, le - lb, stream);
   if (e != hipSuccess) return hip_fail(e, "gather copy kernel launch");
   return HISPARSE_OK;
 }
@@ -671,7 +672,7 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t
   if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[L], 0);
   if (e != hipSuccess) return hip_fail(e, "entry event");
   for (int l = 0; l < L; ++l) {
-    rc = launch_copy(pool, ps, batch, l, l + 1, stats);
+    rc = launch_copy(pool, ps, batch, l, l + 1, stats, 0, true);
     if (rc != HISPARSE_OK) return rc;
     e = hipEventRecord(ev[l], ps);
     if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[l], 0);

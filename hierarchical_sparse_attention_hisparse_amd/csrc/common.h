@@ -35,6 +35,11 @@ constexpr int kCopyThreads = 256;
 constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
 constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
 constexpr int kCopyRowsInFlight = 4;  // rows per wavefront per iteration of the fused copy
+constexpr int kNarrowCopyThreads = 1024;  // narrow copy (beside decode): threads per workgroup
+#ifndef HISPARSE_NARROW_COPY_GROUPS
+#define HISPARSE_NARROW_COPY_GROUPS 32
+#endif
+constexpr int kNarrowCopyGroups = HISPARSE_NARROW_COPY_GROUPS;  // and workgroups, so decode keeps the other CUs
 
 // Invalidation by host rows: sets up to this many rows are searched in LDS.
 constexpr int kInvalidateLdsRows = 8192;

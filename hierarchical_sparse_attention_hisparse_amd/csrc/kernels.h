@@ -97,6 +97,9 @@ struct InvalidateParams {
 hipError_t prepare_resolve(size_t lds_bytes);
 hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream);
 hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream);
+// The same copy on at most `groups` workgroups of 1024 threads.
+hipError_t launch_gather_copy_narrow(const CopyParams& p, int batch, int layers, int groups,
+                                     hipStream_t stream);
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
 hipError_t prepare_sparse_mla_decode();
 size_t decode_lds_bytes();
