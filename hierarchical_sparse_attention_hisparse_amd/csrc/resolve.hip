@@ -39,6 +39,26 @@ constexpr uint64_t kEmptyCell = ~0ull;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memory
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// N consecutive int32 from `base` as 16-byte (or N*4-byte) vector loads; the
+// caller guarantees the alignment.
+template <int N>
+__device__ inline void load_run(const int32_t* base, int (&v)[N]) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const i32x4 x = ((const i32x4*)base)[q];
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
+  } else if constexpr (N == 2) {
+    const i32x2 x = *(const i32x2*)base;
+    v[0] = x.x; v[1] = x.y;
+  } else {
+    v[0] = base[0];
+  }
+}
 
 __device__ inline int lane_prefix(uint64_t m) {  // popcount of m below this lane
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -160,17 +180,21 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   const int r = p.req_idx[b];
   const int nraw = p.seq_lens[b];
 
-  // This thread's top-k entries, loaded before anything depends on r.  The
-  // loads use clamped (always in-range) indices so that they issue back to
-  // back without per-load branches; out-of-range lanes discard the value.
+  // This thread's top-k entries, loaded before anything depends on r: one
+  // vector run when the row allows it, else loads at clamped (always
+  // in-range) indices that issue back to back without per-load branches.
+  // Entries past k hold copies and are skipped wherever used.
   const int i0 = tid * KPT;
-  // Lanes past k hold a copy of entry k-1 and are skipped wherever used.
   int tr[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) tr[j] = -1;
   if (k > 0) {
+    if (p.vec_topk) {
+      load_run<KPT>(tk + min(i0, k - KPT), tr);
+    } else {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) tr[j] = tk[min(i0 + j, k - 1)];
+      for (int j = 0; j < KPT; ++j) tr[j] = tk[min(i0 + j, k - 1)];
+    }
   }
 
   if (r < 0 || r >= p.R) {  // padding row
@@ -222,11 +246,17 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // of slot S-1 and are excluded wherever used.
   const int s0 = tid * SPT;
   int sr[SPT], lr[SPT];
+  if (p.vec_state) {  // S % SPT == 0 and aligned rows: two vector runs
+    const int sv = min(s0, S - SPT);
+    load_run<SPT>(st + sv, sr);
+    load_run<SPT>(lru + sv, lr);
+  } else {
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int s = min(s0 + j, S - 1);
-    sr[j] = st[s];
-    lr[j] = lru[s];
+    for (int j = 0; j < SPT; ++j) {
+      const int s = min(s0 + j, S - 1);
+      sr[j] = st[s];
+      lr[j] = lru[s];
+    }
   }
 
   // Block-table entries of this thread's positions, at in-range indices,
@@ -564,6 +594,12 @@ hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream) {
   const size_t lds = p.lds.total;
   const int spt = resolve_slots_per_thread(p.S);
   const int kpt = resolve_entries_per_thread(p.k);
+  auto aligned = [](const void* q, int per) {
+    const uintptr_t a = (uintptr_t)4 * (uintptr_t)(per < 4 ? per : 4);
+    return ((uintptr_t)q % a) == 0;
+  };
+  p.vec_topk = (p.k > 0 && p.k % kpt == 0 && aligned(p.topk, kpt)) ? 1 : 0;
+  p.vec_state = (p.S % spt == 0 && aligned(p.st, spt) && aligned(p.lru, spt)) ? 1 : 0;
   switch (spt) {
     case 1: return launch_k<1>(p, batch, lds, stream, kpt);
     case 2: return launch_k<2>(p, batch, lds, stream, kpt);
