@@ -209,7 +209,8 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
     return fail(HISPARSE_EINVAL, "slots %d outside [1, %d]", c.slots, kMaxSlots);
   if (c.max_top_k <= 0 || c.max_top_k > c.slots || c.max_top_k > kMaxTopK)
     return fail(HISPARSE_EINVAL, "max_top_k %d outside [1, min(slots, %d)]", c.max_top_k, kMaxTopK);
-  if (c.max_batch <= 0) return fail(HISPARSE_EINVAL, "max_batch must be > 0");
+  if (c.max_batch <= 0 || c.max_batch > 65535)
+    return fail(HISPARSE_EINVAL, "max_batch %d outside [1, 65535]", c.max_batch);
   if (c.row_bytes <= 0 || c.row_bytes % 16 != 0)
     return fail(HISPARSE_EINVAL, "row_bytes %d is not a positive multiple of 16", c.row_bytes);
   if (c.num_layers <= 0) return fail(HISPARSE_EINVAL, "num_layers must be > 0");

@@ -431,36 +431,47 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
 
 // Combine the splits of every (batch row, head): O = sum_j w_j l_j O_j /
 // sum_j w_j l_j with w_j = 2^(m_j - max m), O_j the normalised partials.
-// One thread per 8 output dims.
+// One thread per 8 output dims; grid.y is the batch row, so every index is
+// 32-bit shifts and masks.  All splits' (m, l) pairs and partial rows (at
+// most NSMAX) are loaded before any is combined.
+template <int NSMAX>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.batch * p.heads * (kLat / 8);
-  if (idx >= total) return;
-  const int q = (int)(idx % (kLat / 8));
-  const int64_t bh = idx / (kLat / 8);
-  const int h = (int)(bh % p.heads);
-  const int b = (int)(bh / p.heads);
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;  // over heads x (kLat / 8)
+  const int h = t / (kLat / 8), q = t % (kLat / 8);
+  if (h >= p.heads) return;
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  const int hg = h / kHeadsPerGroup, hl = h - hg * kHeadsPerGroup;
+  const int hg = h / kHeadsPerGroup, hl = h % kHeadsPerGroup;
   const int NS = p.splits;
   const int64_t e0 = ((int64_t)(b * HG + hg) * NS) * kHeadsPerGroup + hl;
+  f32x2 ml[NSMAX];
+  uint4 v[NSMAX];
   float M = -INFINITY;
-  for (int j = 0; j < NS; ++j) M = fmaxf(M, p.part_ml[2 * (e0 + (int64_t)j * kHeadsPerGroup)]);
+#pragma unroll
+  for (int j = 0; j < NSMAX; ++j) {
+    ml[j] = f32x2{-INFINITY, 0.f};
+    v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < NS) {
+      const int64_t e = e0 + (int64_t)j * kHeadsPerGroup;
+      ml[j] = *(const f32x2*)(p.part_ml + 2 * e);
+      v[j] = *(const uint4*)(p.part_o + e * kLat + 8 * q);
+    }
+    M = fmaxf(M, ml[j].x);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int j = 0; j < NS; ++j) {
-      const int64_t e = e0 + (int64_t)j * kHeadsPerGroup;
-      const float m = p.part_ml[2 * e];
-      if (m == -INFINITY) continue;
-      const float wl = exp2f(m - M) * p.part_ml[2 * e + 1];
-      L += wl;
-      const uint4 v = *(const uint4*)(p.part_o + e * kLat + 8 * q);
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[2 * k] += wl * __uint_as_float(wd[k] << 16);
-        acc[2 * k + 1] += wl * __uint_as_float(wd[k] & 0xFFFF0000u);
+    for (int j = 0; j < NSMAX; ++j) {
+      if (j < NS && ml[j].x != -INFINITY) {
+        const float wl = exp2f(ml[j].x - M) * ml[j].y;
+        L += wl;
+        const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += wl * __uint_as_float(wd[k] << 16);
+          acc[2 * k + 1] += wl * __uint_as_float(wd[k] & 0xFFFF0000u);
+        }
       }
     }
   }
@@ -504,9 +515,17 @@ hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_
   hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(grid), dim3(256), decode_lds_bytes(), stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = (int64_t)batch * p.heads * (kLat / 8);
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, p);
+  const int per_row = p.heads * (kLat / 8);
+  const dim3 cgrid((unsigned)((per_row + 255) / 256), (unsigned)batch);
+  static_assert(kMaxDecodeSplits <= 16, "combine instances");
+  if (p.splits <= 2)
+    hipLaunchKernelGGL(decode_combine_kernel<2>, cgrid, dim3(256), 0, stream, p);
+  else if (p.splits <= 4)
+    hipLaunchKernelGGL(decode_combine_kernel<4>, cgrid, dim3(256), 0, stream, p);
+  else if (p.splits <= 8)
+    hipLaunchKernelGGL(decode_combine_kernel<8>, cgrid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<16>, cgrid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ typedef struct {
                              for a pair that does not fit.  S=4096, k=2048
                              needs 101 KB; S=6144, k=2048 103 KB; S=16384
                              allows k up to 1024.                               */
-  int32_t max_batch;      /* largest batch of any call (sizes the miss plan)     */
+  int32_t max_batch;      /* largest batch of any call (sizes the miss plan),
+                             1..65535                                           */
   int32_t row_bytes;      /* bytes per KV row, a multiple of 16 (656 for the
                              fp8 sparse-MLA row)                                 */
   int32_t num_layers;     /* L >= 1 layers that share one index and one plan    */
