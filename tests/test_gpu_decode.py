@@ -42,8 +42,10 @@ def _run_decode(dev_pool, locs_np, q, heads, max_top_k):
         hb.free()
 
 
+# Key splits per row at these shapes: 3, 2, 2, 10, 4, 16 and 8, so the split
+# combine runs at each of its unrolled widths (2, 4, 8, 16).
 @pytest.mark.parametrize("B,H,k", [(5, 32, 77), (3, 16, 33), (2, 48, 64), (4, 128, 300),
-                                   (3, 256, 100), (1, 128, 2048)])
+                                   (3, 256, 100), (1, 128, 2048), (32, 64, 256)])
 def test_decode_small_vs_oracle(B, H, k):
     print("[decode] B=%d H=%d k=%d" % (B, H, k), flush=True)
     rows = max(900, k + 64)
