@@ -68,7 +68,7 @@ struct ResolveLds {
   int hash_size;   // cells of the open-addressing table (power of two >= 2k)
   int sort_size;   // power of two >= S (fallback sort)
   size_t off_hash, off_ehit, off_sort;
-  size_t off_etok, off_mentry, off_victim, off_flag, off_scratch;
+  size_t off_etok, off_mentry, off_mhost, off_victim, off_scratch;
   size_t total;
 };
 
@@ -96,8 +96,8 @@ __host__ __device__ inline ResolveLds resolve_lds_layout_f(int S, int k, int fac
   o = end_hash > end_sort ? end_hash : end_sort;
   L.off_etok = o;    o = align16(o + 4 * (size_t)k);
   L.off_mentry = o;  o = align16(o + 4 * (size_t)k);
+  L.off_mhost = o;   o = align16(o + 8 * (size_t)k);
   L.off_victim = o;  o = align16(o + 4 * (size_t)k);
-  L.off_flag = o;    o = align16(o + (size_t)S);
   L.off_scratch = o; o = align16(o + 4 * (size_t)kResolveScratchInts);
   L.total = o;
   return L;

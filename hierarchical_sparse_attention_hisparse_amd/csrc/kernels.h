@@ -26,10 +26,9 @@ struct ResolveParams {
   int32_t* plan_cnt;
   int32_t plan_stride;
   ResolveLds lds;  // LDS carve-up for (S, k), filled in by launch_resolve
-  // Vector loads of whole per-thread runs (set by launch_resolve): the top-k
-  // row when k % entries-per-thread == 0 and the pointer is aligned; the
-  // slot-state rows likewise for slots-per-thread.
-  int32_t vec_topk, vec_state;
+  // Vector loads of each thread's slot-state run (set by launch_resolve):
+  // S % slots-per-thread == 0 and the rows aligned for them.
+  int32_t vec_state;
   // Fused miss copy (copy_layers > 0): after planning, the workgroup copies
   // its own misses into layers [0, copy_layers) itself.  The per-layer
   // pointers travel in the kernel arguments (constant, scalar-loaded).

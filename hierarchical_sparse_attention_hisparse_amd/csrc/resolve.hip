@@ -169,7 +169,8 @@ enum : int {
 static_assert(kScrInts == kResolveScratchInts, "scratch layout");
 
 // COPY: the workgroup also copies its misses into p.copy_layers layers.
-template <int SPT, int KPT, bool COPY>
+// VEC: each thread's slot-state run is loaded as vectors.
+template <int SPT, int KPT, bool COPY, bool VEC>
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -180,21 +181,17 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   const int r = p.req_idx[b];
   const int nraw = p.seq_lens[b];
 
-  // This thread's top-k entries, loaded before anything depends on r: one
-  // vector run when the row allows it, else loads at clamped (always
-  // in-range) indices that issue back to back without per-load branches.
-  // Entries past k hold copies and are skipped wherever used.
+  // This thread's top-k entries, loaded before anything depends on r.  The
+  // loads use clamped (always in-range) indices so that they issue back to
+  // back without per-load branches; entries past k hold a copy of entry k-1
+  // and are skipped wherever used.
   const int i0 = tid * KPT;
   int tr[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) tr[j] = -1;
   if (k > 0) {
-    if (p.vec_topk) {
-      load_run<KPT>(tk + min(i0, k - KPT), tr);
-    } else {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) tr[j] = tk[min(i0 + j, k - 1)];
-    }
+    for (int j = 0; j < KPT; ++j) tr[j] = tk[min(i0 + j, k - 1)];
   }
 
   if (r < 0 || r >= p.R) {  // padding row
@@ -246,7 +243,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // of slot S-1 and are excluded wherever used.
   const int s0 = tid * SPT;
   int sr[SPT], lr[SPT];
-  if (p.vec_state) {  // S % SPT == 0 and aligned rows: two vector runs
+  // VEC (S % SPT == 0, aligned rows): two vector runs.  A separate instance,
+  // not a branch: merging the two load paths would make the compiler wait
+  // for the loads at the merge.
+  if constexpr (VEC) {
     const int sv = min(s0, S - SPT);
     load_run<SPT>(st + sv, sr);
     load_run<SPT>(lru + sv, lr);
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int32_t* e_tok = (int32_t*)(smem + L.off_etok);
   int32_t* m_entry = (int32_t*)(smem + L.off_mentry);
   int32_t* victim = (int32_t*)(smem + L.off_victim);
-  uint8_t* s_flag = (uint8_t*)(smem + L.off_flag);
+  int64_t* m_h = (int64_t*)(smem + L.off_mhost);     // host row of the j-th miss
   uint64_t* s_sort = (uint64_t*)(smem + L.off_sort);
   const int HS = L.hash_size;
   const int hshift = 32 - ilog2(HS);
@@ -286,9 +286,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (i0 + j < k) e_hit[i0 + j] = INT_MAX;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j)
-    if (s0 + j < S) s_flag[s0 + j] = 0;
   // Barriers below order LDS only: no thread reads global memory that another
   // thread of the workgroup wrote, so the slot-state loads stay in flight
   // through step 1 and the row-ID and stamp stores never hold a barrier.
@@ -329,6 +326,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 
   // Step 2: probe the table with every slot's token; the SPT probes of a
   // thread advance together so a wavefront waits for its longest chain once.
+  int hidx[SPT];  // top-k index of the pending entry this slot's token matches, or -1
   {
     uint32_t hh[SPT];
     uint64_t hv[SPT];
@@ -356,27 +354,33 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         }
     }
 #pragma unroll
-    for (int j = 0; j < SPT; ++j)
-      if ((live & (1u << j)) && hv[j] != kEmptyCell) atomicMin(&e_hit[(int)(uint32_t)hv[j]], s0 + j);
+    for (int j = 0; j < SPT; ++j) {
+      hidx[j] = ((live & (1u << j)) && hv[j] != kEmptyCell) ? (int)(uint32_t)hv[j] : -1;
+      if (hidx[j] >= 0) atomicMin(&e_hit[hidx[j]], s0 + j);
+    }
   }
   lds_barrier();
 
-  // Step 3: hits and the ordered miss list.
+  // Step 3: hits and the ordered miss list.  A miss's host row is loaded as
+  // soon as the miss is known; it travels with the list.
+  const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
   int n_hit = 0, my_miss = 0;
   unsigned missbits = 0;
+  int64_t hm[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
+    hm[j] = -1;
     if (!(pend & (1u << j))) continue;
     const int i = i0 + j;
     const int s = e_hit[i];
     if (s != INT_MAX) {
       outb[i] = rowbase + s;
       lru[s] = c;
-      s_flag[s] = 1;
       ++n_hit;
     } else {
       missbits |= 1u << j;
       ++my_miss;
+      hm[j] = locr[tr[j]];
     }
   }
   {
@@ -391,9 +395,45 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   }
   int m_total;
   int mpos = block_exscan_small<bits_for(KPT)>(my_miss, scr + kScrMiss, &m_total);
+  // Slots: the hit slot of an entry is the one that entry's e_hit names.
+  unsigned hitm = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if (hidx[j] >= 0 && e_hit[hidx[j]] == s0 + j) hitm |= 1u << j;
+
+  // The miss list; the fused instance also needs the host rows now (for the
+  // rows loaded ahead), the plan-only instance writes them after the victims
+  // are ranked, so the loads never hold a barrier.
+  const int mpos0 = mpos;
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
-    if (missbits & (1u << j)) m_entry[mpos++] = i0 + j;
+    if (missbits & (1u << j)) {
+      if (COPY) m_h[mpos] = hm[j];
+      m_entry[mpos++] = i0 + j;
+    }
+
+  // Fused copy, first rows: each wavefront loads its first kCopyRowsInFlight
+  // rows of the first layer now, so the host link already works while the
+  // victims are ranked; they are stored once their slots are known.
+  constexpr int RIF = kCopyRowsInFlight;
+  u32x4 pre[RIF];
+  const bool have_pre = COPY && m_total > 0 && p.units <= kWave;
+  if (have_pre) {
+    lds_barrier();  // the miss list of every wavefront
+#pragma unroll
+    for (int q = 0; q < RIF; ++q) {
+      pre[q] = u32x4{0u, 0u, 0u, 0u};
+      const int j = wid + q * kResolveWaves;
+      if (j < m_total) {
+        const int64_t hv = m_h[j];
+        const int64_t h = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)hv) |
+                          ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(hv >> 32)) << 32);
+        const bool ok = h >= 0 && h < p.host_rows[0];
+        const gu4* src = ok ? (const gu4*)p.host_pool[0] + h * p.units : (const gu4*)p.zero_row;
+        if (lane < p.units) pre[q] = src[lane];
+      }
+    }
+  }
 
   // Step 4: victims, in (occupied, stamp, slot) order among non-hit slots.
   uint64_t key[SPT];
@@ -401,7 +441,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     key[j] = ((uint64_t)(sr[j] >= 0 ? 1u : 0u) << 32) | (uint64_t)((uint32_t)lr[j] ^ 0x80000000u);
-    if (s0 + j < S && s_flag[s0 + j] == 0) cand |= 1u << j;
+    if (s0 + j < S && !(hitm & (1u << j))) cand |= 1u << j;
   }
   int need = m_total, vbase = 0;
 #pragma unroll 1
@@ -461,13 +501,18 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       victim[vbase + j] = s < S ? s : S - 1;  // always < S: candidates >= misses
     }
   }
+  if (!COPY) {
+    int mp = mpos0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (missbits & (1u << j)) m_h[mp++] = hm[j];
+  }
   lds_barrier();
 
   // Step 5: the j-th miss takes the j-th victim; emit the compact plan.  The
   // fused copy keeps its own copy of the plan in the (now dead) table region.
   int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
   int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
-  const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
   int64_t* f_src = (int64_t*)(smem + L.off_hash);          // [k]
   int32_t* f_dst = (int32_t*)(smem + L.off_hash + 8 * (size_t)k);  // [k]
   for (int j = tid; j < m_total; j += kResolveThreads) {
@@ -478,7 +523,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     lru[s] = c;
     const int row = rowbase + s;
     outb[i] = row;
-    const int64_t h = locr[t];
+    const int64_t h = m_h[j];
     psrc[j] = h;
     pdst[j] = row;
     if (COPY) {
@@ -497,12 +542,12 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int copy_trips = 0;
   if (COPY && m_total > 0) {
     lds_barrier();
-    constexpr int RIF = kCopyRowsInFlight;
     const int U = p.units;
     const int total = m_total * p.copy_layers;
     const int wu = __builtin_amdgcn_readfirstlane(wid);
 #pragma unroll 1
     for (int u = wu; u < total; u += RIF * kResolveWaves) {
+      const bool first = u == wu;
       const gu4* src[RIF];
       gu4* dst[RIF];
 #pragma unroll
@@ -521,7 +566,11 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       for (int part = lane; part < U; part += kWave) {
         u32x4 v[RIF];
 #pragma unroll
-        for (int q = 0; q < RIF; ++q) v[q] = src[q][part];
+        for (int q = 0; q < RIF; ++q) {
+          // rows of the first layer that were loaded ahead (one unit per lane)
+          if (have_pre && first && u + q * kResolveWaves < m_total) v[q] = pre[q];
+          else v[q] = src[q][part];
+        }
 #pragma unroll
         for (int q = 0; q < RIF; ++q) dst[q][part] = v[q];
       }
@@ -549,12 +598,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 
 template <int SPT, int KPT>
 hipError_t launch_t(const ResolveParams& p, int batch, size_t lds, hipStream_t stream) {
-  if (p.copy_layers > 0)
-    hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true>), dim3(batch), dim3(kResolveThreads), lds,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false>), dim3(batch), dim3(kResolveThreads), lds,
-                       stream, p);
+  const dim3 g(batch), t(kResolveThreads);
+  if (p.copy_layers > 0) {
+    if (p.vec_state) hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true, true>), g, t, lds, stream, p);
+    else hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true, false>), g, t, lds, stream, p);
+  } else {
+    if (p.vec_state) hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false, true>), g, t, lds, stream, p);
+    else hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false, false>), g, t, lds, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -570,11 +621,16 @@ hipError_t launch_k(const ResolveParams& p, int batch, size_t lds, hipStream_t s
 
 template <int SPT, int KPT>
 hipError_t set_attr() {
-  hipError_t e = hipFuncSetAttribute((const void*)resolve_kernel<SPT, KPT, false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)resolve_kernel<SPT, KPT, true>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+  const void* fns[4] = {(const void*)resolve_kernel<SPT, KPT, false, false>,
+                        (const void*)resolve_kernel<SPT, KPT, false, true>,
+                        (const void*)resolve_kernel<SPT, KPT, true, false>,
+                        (const void*)resolve_kernel<SPT, KPT, true, true>};
+  for (const void* f : fns) {
+    const hipError_t e =
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int SPT>
@@ -598,7 +654,6 @@ hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream) {
     const uintptr_t a = (uintptr_t)4 * (uintptr_t)(per < 4 ? per : 4);
     return ((uintptr_t)q % a) == 0;
   };
-  p.vec_topk = (p.k > 0 && p.k % kpt == 0 && aligned(p.topk, kpt)) ? 1 : 0;
   p.vec_state = (p.S % spt == 0 && aligned(p.st, spt) && aligned(p.lru, spt)) ? 1 : 0;
   switch (spt) {
     case 1: return launch_k<1>(p, batch, lds, stream, kpt);

@@ -72,12 +72,12 @@ typedef struct {
                              1..16384                                           */
   int32_t max_top_k;      /* largest top_k of any call, 1..S and <= 4096.  The
                              resolver keeps one request's table in 160 KB of
-                             LDS, about max(8*pow2(4k) + 4k, 8*pow2(S)) + 12k
-                             + S bytes (the table drops to 2 cells per entry
+                             LDS, about max(8*pow2(4k) + 4k, 8*pow2(S)) + 20k
+                             bytes (the table drops to 2 cells per entry
                              when 4 do not fit); init returns EUNSUPPORTED
-                             for a pair that does not fit.  S=4096, k=2048
-                             needs 101 KB; S=6144, k=2048 103 KB; S=16384
-                             allows k up to 1024.                               */
+                             for a pair that does not fit.  S=4096 or 6144
+                             with k=2048 needs 113 KB; S <= 8192 allows k up
+                             to 4048, S=16384 up to 1580.                       */
   int32_t max_batch;      /* largest batch of any call (sizes the miss plan),
                              1..65535                                           */
   int32_t row_bytes;      /* bytes per KV row, a multiple of 16 (656 for the
