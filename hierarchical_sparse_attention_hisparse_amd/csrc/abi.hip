@@ -236,7 +236,8 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
     return fail(HISPARSE_EINVAL, "pool arrays are NULL");
   const int L = c.num_layers;
   for (int l = 0; l < L; ++l) {
-    if (host_pool_rows[l] < 0) return fail(HISPARSE_EINVAL, "host_pool_rows[%d] < 0", l);
+    if (host_pool_rows[l] < 0 || host_pool_rows[l] > INT32_MAX)
+      return fail(HISPARSE_EINVAL, "host_pool_rows[%d] outside [0, 2^31)", l);
     if (host_pool_rows[l] > 0 && (!host_pools[l] || !aligned(host_pools[l], 16)))
       return fail(HISPARSE_EINVAL, "host_pools[%d] is NULL or not 16-byte aligned", l);
     if (!device_pools[l] || !aligned(device_pools[l], 16))

@@ -96,7 +96,7 @@ __host__ __device__ inline ResolveLds resolve_lds_layout_f(int S, int k, int fac
   o = end_hash > end_sort ? end_hash : end_sort;
   L.off_etok = o;    o = align16(o + 4 * (size_t)k);
   L.off_mentry = o;  o = align16(o + 4 * (size_t)k);
-  L.off_mhost = o;   o = align16(o + 8 * (size_t)k);
+  L.off_mhost = o;   o = align16(o + 4 * (size_t)k);
   L.off_victim = o;  o = align16(o + 4 * (size_t)k);
   L.off_scratch = o; o = align16(o + 4 * (size_t)kResolveScratchInts);
   L.total = o;

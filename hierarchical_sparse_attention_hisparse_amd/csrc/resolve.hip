@@ -277,7 +277,9 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int32_t* e_tok = (int32_t*)(smem + L.off_etok);
   int32_t* m_entry = (int32_t*)(smem + L.off_mentry);
   int32_t* victim = (int32_t*)(smem + L.off_victim);
-  int64_t* m_h = (int64_t*)(smem + L.off_mhost);     // host row of the j-th miss
+  // Host row of the j-th miss.  Host pools hold fewer than 2^31 rows (checked
+  // at init), so a row outside [0, 2^31) is kept as -1: out of range either way.
+  int32_t* m_h = (int32_t*)(smem + L.off_mhost);
   uint64_t* s_sort = (uint64_t*)(smem + L.off_sort);
   const int HS = L.hash_size;
   const int hshift = 32 - ilog2(HS);
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
   int n_hit = 0, my_miss = 0;
   unsigned missbits = 0;
-  int64_t hm[KPT];
+  int32_t hm[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     hm[j] = -1;
@@ -380,7 +382,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     } else {
       missbits |= 1u << j;
       ++my_miss;
-      hm[j] = locr[tr[j]];
+      const int64_t h = locr[tr[j]];
+      hm[j] = (h >= 0 && h <= INT_MAX) ? (int32_t)h : -1;
     }
   }
   {
@@ -425,9 +428,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       pre[q] = u32x4{0u, 0u, 0u, 0u};
       const int j = wid + q * kResolveWaves;
       if (j < m_total) {
-        const int64_t hv = m_h[j];
-        const int64_t h = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)hv) |
-                          ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(hv >> 32)) << 32);
+        const int64_t h = __builtin_amdgcn_readfirstlane(m_h[j]);
         const bool ok = h >= 0 && h < p.host_rows[0];
         const gu4* src = ok ? (const gu4*)p.host_pool[0] + h * p.units : (const gu4*)p.zero_row;
         if (lane < p.units) pre[q] = src[lane];
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     lru[s] = c;
     const int row = rowbase + s;
     outb[i] = row;
-    const int64_t h = m_h[j];
+    const int64_t h = m_h[j];  // -1 for a row outside [0, 2^31)
     psrc[j] = h;
     pdst[j] = row;
     if (COPY) {

@@ -72,12 +72,12 @@ typedef struct {
                              1..16384                                           */
   int32_t max_top_k;      /* largest top_k of any call, 1..S and <= 4096.  The
                              resolver keeps one request's table in 160 KB of
-                             LDS, about max(8*pow2(4k) + 4k, 8*pow2(S)) + 20k
+                             LDS, about max(8*pow2(4k) + 4k, 8*pow2(S)) + 16k
                              bytes (the table drops to 2 cells per entry
                              when 4 do not fit); init returns EUNSUPPORTED
                              for a pair that does not fit.  S=4096 or 6144
-                             with k=2048 needs 113 KB; S <= 8192 allows k up
-                             to 4048, S=16384 up to 1580.                       */
+                             with k=2048 needs 105 KB; S <= 8192 allows k up
+                             to 4096, S=16384 up to 1976.                       */
   int32_t max_batch;      /* largest batch of any call (sizes the miss plan),
                              1..65535                                           */
   int32_t row_bytes;      /* bytes per KV row, a multiple of 16 (656 for the
@@ -110,7 +110,8 @@ int hisparse_host_free(void* ptr);
  *   host_pools[L]      host: pinned host pool of layer l, host_pool_rows[l]
  *                      rows of row_bytes each (rows addressed by
  *                      host_cache_locs).
- *   host_pool_rows[L]  host: row counts of the host pools.
+ *   host_pool_rows[L]  host: row counts of the host pools, each < 2^31
+ *                      (1.4 TB of 656-byte rows per layer).
  *   device_pools[L]    device: one row pool per layer, device_pool_rows rows of
  *                      row_bytes, 16-byte aligned.  Resident and hot rows share
  *                      it ("vLLM Hybrid HiSparse 源码实现分析" section 2.2):

@@ -141,6 +141,36 @@ def test_corrupt_state_and_tripwires(mode, layers):
         pair.close()
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("S,k", [(4096, 4096), (8192, 4096), (16384, 1976)])
+def test_lds_budget_corners(mode, S, k):
+    """The largest slot / top-k pairs the LDS budget allows: the table with
+    two cells per entry, 4 and 8 top-k entries and 4, 8 and 16 slots per
+    thread.  After the cold step the stamps are scrambled, so step 1 ranks
+    its victims through the full sort over every slot."""
+    print("[corner %s] S=%d k=%d" % (mode, S, k), flush=True)
+    n0 = [2 * S + 7, 3 * S, 2 * S + 100, 4 * S, 2 * S + 33, 3 * S - 1, 5 * S, 2 * S + 1]
+    w = synth("corner", 29, R=8, S=S, k=k, steps=3, n0=n0, keep=(3 * k) // 4)
+    bufs = make_host_pools(w)
+    pair = Pair(w, bufs, mode=mode)
+    try:
+        rng = np.random.default_rng(9)
+        for step in range(w.steps):
+            if step == 1:
+                lru = (rng.permutation(w.R * w.S).reshape(w.R, w.S) - 1000).astype(np.int32)
+                pair.lru.copy_(torch.from_numpy(lru))
+                pair.ost.lru_slots[:] = lru
+            dst, src = pair.gpu_step(step)
+            o = pair.oracle_step(step, dst, src)
+            torch.cuda.synchronize()
+            pair.compare_step(step, o)
+            print("[corner %s] S=%d k=%d step %d ok" % (mode, S, k, step), flush=True)
+        pair.compare_pools()
+        assert pair.ost.stats[1] > 0
+    finally:
+        pair.close()
+
+
 def test_host_side_errors():
     w = synth("err", 27, R=2, S=64, k=8, steps=1, n0=[500, 100])
     bufs = make_host_pools(w)
