@@ -64,31 +64,60 @@ __global__ __launch_bounds__(256) void invalidate_tokens_kernel(InvalidateParams
   }
 }
 
-// One thread per slot of every request row: the slot's host row is looked
-// up in the sorted set (staged in LDS when it fits) by binary search.
-__global__ __launch_bounds__(256) void invalidate_host_rows_kernel(InvalidateParams p) {
+// kInvSlotsPerThread consecutive slots (of the flattened [R][S] state) per
+// thread, kInvThreads threads per workgroup; the sorted set is staged in LDS
+// once per workgroup.  Each slot's host row is looked up with a branch-free
+// lower bound of a fixed step count; a thread's searches advance together.
+// Measured on 72 requests x 4096 slots against 4096 rows: 512 x 1 takes
+// 9.6 us, 256 x 1 11.5, 1024 x 1 9.8, 512 x 2 11.8, 1024 x 4 15.3.
+#ifndef HISPARSE_INV_THREADS
+#define HISPARSE_INV_THREADS 512
+#endif
+#ifndef HISPARSE_INV_SLOTS
+#define HISPARSE_INV_SLOTS 1
+#endif
+constexpr int kInvThreads = HISPARSE_INV_THREADS;
+constexpr int kInvSlotsPerThread = HISPARSE_INV_SLOTS;
+
+__device__ inline int lower_bound_fixed(const int64_t* rows, int count, int64_t h) {
+  int base = 0, n = count;
+  while (n > 1) {
+    const int half = n >> 1;
+    base = rows[base + half] < h ? base + half : base;
+    n -= half;
+  }
+  return base + (rows[base] < h ? 1 : 0);
+}
+
+__global__ __launch_bounds__(kInvThreads) void invalidate_host_rows_kernel(InvalidateParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   int64_t* srows = (int64_t*)smem;
   const bool staged = p.count <= kInvalidateLdsRows;
   if (staged)
-    for (int j = threadIdx.x; j < p.count; j += 256) srows[j] = p.rows[j];
+    for (int j = threadIdx.x; j < p.count; j += kInvThreads) srows[j] = p.rows[j];
   __syncthreads();
-  const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (slot >= (int64_t)p.R * p.S) return;
-  const int r = (int)(slot / p.S);
-  const int t = p.slot_tokens[slot];
-  if (t < 0 || (int64_t)t >= p.max_seq_len) return;
-  const int64_t h = p.host_cache_locs[(int64_t)r * p.max_seq_len + t];
   const int64_t* rows = staged ? srows : p.rows;
-  int lo = 0, hi = p.count;  // first index with rows[idx] >= h
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (rows[mid] < h) lo = mid + 1;
-    else hi = mid;
+  const int64_t total = (int64_t)p.R * p.S;
+  const int64_t s0 = ((int64_t)blockIdx.x * kInvThreads + threadIdx.x) * kInvSlotsPerThread;
+  int64_t h[kInvSlotsPerThread];
+  bool live[kInvSlotsPerThread];
+#pragma unroll
+  for (int q = 0; q < kInvSlotsPerThread; ++q) {
+    const int64_t slot = s0 + q;
+    const int64_t sc = slot < total ? slot : total - 1;  // in-range index for every load
+    const int t = p.slot_tokens[sc];
+    live[q] = slot < total && t >= 0 && (int64_t)t < p.max_seq_len;
+    const int r = (int)(sc / p.S);
+    h[q] = p.host_cache_locs[(int64_t)r * p.max_seq_len + (live[q] ? t : 0)];
   }
-  if (lo < p.count && rows[lo] == h) {
-    p.slot_tokens[slot] = -1;
-    p.lru_slots[slot] = 0;
+#pragma unroll
+  for (int q = 0; q < kInvSlotsPerThread; ++q) {
+    if (!live[q]) continue;
+    const int idx = lower_bound_fixed(rows, p.count, h[q]);
+    if (idx < p.count && rows[idx] == h[q]) {
+      p.slot_tokens[s0 + q] = -1;
+      p.lru_slots[s0 + q] = 0;
+    }
   }
 }
 
@@ -112,9 +141,10 @@ hipError_t launch_invalidate_tokens(const InvalidateParams& p, hipStream_t strea
 hipError_t launch_invalidate_host_rows(const InvalidateParams& p, hipStream_t stream) {
   if (p.count <= 0) return hipSuccess;
   const int64_t slots = (int64_t)p.R * p.S;
+  const int64_t per_block = (int64_t)kInvThreads * kInvSlotsPerThread;
   const size_t lds = p.count <= kInvalidateLdsRows ? (size_t)p.count * sizeof(int64_t) : 0;
-  hipLaunchKernelGGL(invalidate_host_rows_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256),
-                     lds, stream, p);
+  hipLaunchKernelGGL(invalidate_host_rows_kernel, dim3((unsigned)((slots + per_block - 1) / per_block)),
+                     dim3(kInvThreads), lds, stream, p);
   return hipGetLastError();
 }
 
