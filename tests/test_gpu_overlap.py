@@ -16,13 +16,21 @@ pytestmark = pytest.mark.gpu
 SCALE = 1.0 / math.sqrt(192.0)
 
 
-@pytest.mark.parametrize("B", [4, 9])
-def test_overlapped_layers_match_sequential(B):
-    print("[overlap] B=%d" % B, flush=True)
+@pytest.mark.parametrize("B,corrupt", [(4, False), (9, False), (9, True)])
+def test_overlapped_layers_match_sequential(B, corrupt):
+    """With `corrupt`, some host rows are out of range (negative or past the
+    pool), so the narrow copy's zero fill and tripwire count are compared
+    too."""
+    print("[overlap] B=%d corrupt=%s" % (B, corrupt), flush=True)
     L, H = 3, 32
     n0 = [3000 + 700 * b for b in range(B)]
     w = synth("ovl", 70 + B, R=B, S=256, k=128, steps=3, n0=n0, L=L, grow=1, keep=80, recent=16,
               recent_window=64)
+    if corrupt:   # every request is past S, so admission copies no host rows
+        rng = np.random.default_rng(12)
+        locs = w.host_cache_locs
+        locs[rng.random(locs.shape) < 0.04] = -3
+        locs[rng.random(locs.shape) < 0.04] = w.host_pool_rows + 7
     bufs = make_host_pools(w, kind="mla")
     seq = Pair(w, bufs, with_oracle=False)
     ovl = Pair(w, bufs)
@@ -59,6 +67,8 @@ def test_overlapped_layers_match_sequential(B):
             print("[overlap] step %d layer %d max normwise error %.3g" % (step, l, err.max()),
                   flush=True)
             assert err.max() <= 2e-2
+        if corrupt:
+            assert int(ovl.stats[4].item()) > 0
     finally:
         seq.close()
         ovl.close()
