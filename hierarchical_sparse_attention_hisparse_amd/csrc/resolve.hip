@@ -12,7 +12,8 @@
 //   2. each slot holding a pending position marks that entry's hit slot (the
 //      lowest slot if the map was corrupted into duplicates);
 //   3. hits get their row ID and a refreshed stamp; misses are listed in
-//      ascending top-k index;
+//      ascending top-k index with their host rows (loaded as soon as each
+//      miss is known); a slot learns it is a hit slot from its entry;
 //   4. victims: rounds of block-wide minimum over the candidates' (occupied,
 //      stamp) keys, each round taking the slots of the minimum key in slot
 //      order; if a few rounds do not cover every miss, a bitonic LDS sort of
@@ -21,7 +22,9 @@
 //      (host row, device row) entry of the compact miss plan;
 //   6. (COPY instances) the workgroup copies its own misses from the pinned
 //      host pools into every layer, one wavefront per row, so each request's
-//      copy starts as soon as its plan exists and no second launch is needed.
+//      copy starts as soon as its plan exists and no second launch is needed;
+//      each wavefront's first rows are loaded before step 4, so the host link
+//      is busy while the victims are ranked.
 // Resolution order and phases: "vLLM HiSparse 本地 KV 卸载架构" (hot-row lookup
 // and LRU) and "vLLM Hybrid HiSparse 源码实现分析" section 7.2; fast path
 // (seq_len <= S: slot == position, nothing moves): the per-step flow of the
