@@ -11,9 +11,10 @@
 // One workgroup of 4 wavefronts per (batch row, group of 128 heads, split of
 // the keys).  All four wavefronts share the loading: each block of 32 keys is
 // fetched a block ahead into registers, then dequantised (fp8 -> f32, times
-// the scale, RNE to bf16) and written to a double-buffered bf16 tile
+// the scale, RNE to bf16) and written to one of three bf16 tiles
 // [32 keys][576 (+8 pad) dims] in LDS between the MFMAs of the previous
-// block's score loop; one barrier per block.  Each wavefront
+// block's score loop.  With three tiles and two P buffers, the one barrier
+// per block (after P is published) also orders every tile reuse.  Each wavefront
 // computes the scores of its own 32 heads, so every K fragment read from LDS
 // feeds two MFMAs (LDS instruction issue, not bytes, bounds this loop on
 // gfx950), and then O for a quarter of the dims of all 128 heads, so every
@@ -52,8 +53,9 @@ constexpr float kMaxExcessLog2 = 64.f;            // largest score above a head'
 constexpr int kQRopeStrideBytes = 144;            // 64 bf16 + 16 pad: conflict-free b128 reads
 constexpr int kLatSteps = kLat / 32;              // 16 k-steps over the latent
 constexpr int kQKAhead = 2;                       // LDS reads this many MFMA steps ahead
-constexpr size_t kOffFlags = 2 * (size_t)kTileBytes;
-constexpr size_t kOffOvf = kOffFlags + 64;        // int: a score exceeded its reference by > 2^64
+constexpr int kTiles = 3;                         // K/V tiles in flight (read, PV, written)
+constexpr size_t kOffFlags = kTiles * (size_t)kTileBytes;
+constexpr size_t kOffOvf = kOffFlags + 128;       // int: a score exceeded its reference by > 2^64
 constexpr size_t kOffQRope = kOffOvf + 16;        // [128 heads][72 bf16] rope part of Q
 constexpr int kHeadTiles = kHeadsPerGroup / 16;    // 8
 constexpr int kDimTilesPerWave = kLat / 16 / kDecWaves;  // 8: O dims 128w..128w+127
@@ -230,13 +232,16 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
     }
     __syncthreads();
 
+    int tcur = 0;  // tile of block i: i mod kTiles
     for (int i = 0; i < nblk; ++i) {
-      const unsigned char* tile = smem + (i & 1) * kTileBytes;
-      const uint8_t* vf = vflags + 32 * (i & 1);
-      // Block i+1 goes into the other buffer, last read before the previous
-      // barrier (past the end of the split it is written and never read).
-      unsigned char* ntile = smem + ((i + 1) & 1) * kTileBytes;
-      uint8_t* nvf = vflags + 32 * ((i + 1) & 1);
+      const int tnext = tcur == kTiles - 1 ? 0 : tcur + 1;
+      const unsigned char* tile = smem + tcur * kTileBytes;
+      const uint8_t* vf = vflags + 32 * tcur;
+      // Block i+1 goes into the third buffer, last read by block i-2's PV,
+      // which every wave finished before the previous barrier (past the end
+      // of the split it is written and never read).
+      unsigned char* ntile = smem + tnext * kTileBytes;
+      uint8_t* nvf = vflags + 32 * tnext;
       bf16x8 pb[2];
       {
         // S^T = K Q^T: 2 key tiles x 2 head tiles, K fragments shared by both head tiles.
@@ -349,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
       }
       {
         // Publish this wave's P^T fragments (B layout) for the other waves.
-        bf16x8* pbuf = (bf16x8*)(smem + kOffP);
+        bf16x8* pbuf = (bf16x8*)(smem + kOffP + (i & 1) * kPBytes);
         pbuf[(2 * wave) * 64 + lane] = pb[0];
         pbuf[(2 * wave + 1) * 64 + lane] = pb[1];
       }
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
       {
         // O^T += V^T P^T over this wave's 128 dims and all 128 heads: every
         // V^T fragment (read transposed from the row-major tile) feeds 8 MFMAs.
-        const bf16x8* pbuf = (const bf16x8*)(smem + kOffP);
+        const bf16x8* pbuf = (const bf16x8*)(smem + kOffP + (i & 1) * kPBytes);
         bf16x8 pf[kHeadTiles];
 #pragma unroll
         for (int ht = 0; ht < kHeadTiles; ++ht) pf[ht] = pbuf[ht * 64 + lane];
@@ -383,7 +388,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
             o[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[ht], o[ht][t], 0, 0, 0);
         }
       }
-      lds_barrier();  // this block's tile and P are no longer read
+      // No barrier here: the next block writes the third tile and the other
+      // P buffer, and this block's are rewritten only after the next block's
+      // P barrier, which every wave reaches after this PV.
+      tcur = tnext;
     }
     if (ovf) *s_ovf = 1;
     __syncthreads();
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 
 }  // namespace
 
-size_t decode_lds_bytes() { return kOffP + kPBytes; }
+size_t decode_lds_bytes() { return kOffP + 2 * kPBytes; }
 
 int decode_splits(int batch, int heads, int k) {
   const int HG = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
