@@ -55,3 +55,14 @@ def test_binding_rejects_bad_arguments_before_any_device_call():
         _dev(None, torch.int32, (3,), "x")
     assert _dev(None, torch.int32, (3,), "x", allow_none=True) is None
     assert hs.STAT_NAMES[4] == "tripwires"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asked for more it says why and exits
+    before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
