@@ -103,6 +103,26 @@ __device__ inline uint64_t wave_min_key(uint64_t v) {
   return ((uint64_t)want << 32) | m;
 }
 
+// One DPP step of an inclusive wavefront prefix sum: lanes whose source is
+// outside the pattern (or whose row is masked off) add 0.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_add_step(uint32_t v) {
+  return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes: within each row of 16 (row_shr 1,
+// 2, 4, 8), then the last lane of row 0 into row 1 and of row 2 into row 3
+// (row_bcast:15), then lane 31 into rows 2-3 (row_bcast:31).
+__device__ inline uint32_t wave_inclusive_sum(uint32_t v) {
+  v = dpp_add_step<0x111, 0xF>(v);
+  v = dpp_add_step<0x112, 0xF>(v);
+  v = dpp_add_step<0x114, 0xF>(v);
+  v = dpp_add_step<0x118, 0xF>(v);
+  v = dpp_add_step<0x142, 0xA>(v);
+  v = dpp_add_step<0x143, 0xC>(v);
+  return v;
+}
+
 // Sum over the wavefront of small per-lane counts (< 2^BITS), by ballots.
 template <int BITS>
 __device__ inline int wave_sum_small(int v) {
@@ -127,14 +147,11 @@ __device__ inline int block_exscan_small(int c, int* buf, int* total) {
   }
   if (lane == 0) buf[wid] = wt;
   lds_barrier();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kResolveWaves; ++w) {
-    const int v = buf[w];
-    base += (w < wid) ? v : 0;
-    tot += v;
-  }
-  *total = tot;
+  // Lane w holds wave w's total; one prefix sum gives every wave its base
+  // (one LDS read per lane instead of kResolveWaves dependent reads).
+  const uint32_t inc = wave_inclusive_sum(lane < kResolveWaves ? (uint32_t)buf[lane] : 0u);
+  *total = __builtin_amdgcn_readlane((int)inc, 63);
+  const int base = wid > 0 ? __builtin_amdgcn_readlane((int)inc, wid - 1) : 0;
   return base + pre;
 }
 
@@ -145,13 +162,7 @@ __device__ inline uint64_t block_min_key(uint64_t v, uint64_t* buf) {
   const uint64_t wm = wave_min_key(v);
   if (lane == 0) buf[wid] = wm;
   lds_barrier();
-  uint64_t m = buf[0];
-#pragma unroll
-  for (int w = 1; w < kResolveWaves; ++w) {
-    const uint64_t x = buf[w];
-    m = x < m ? x : m;
-  }
-  return m;
+  return wave_min_key(lane < kResolveWaves ? buf[lane] : ~0ull);  // lane w: wave w's minimum
 }
 
 __device__ inline uint32_t hash_pos(int t, int shift) {
@@ -581,20 +592,23 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
 
-  if (tid == 0) {
-    int h = 0, rs = 0, tr2 = 0;
-    for (int w = 0; w < kResolveWaves; ++w) {
-      h += scr[kScrStats + w];
-      rs += scr[kScrStats + 16 + w];
-      tr2 += scr[kScrStats + 32 + w];
-    }
-    p.plan_cnt[b] = m_total;
-    p.clk[r] = c;
-    if (p.stats) {
-      if (h) atomicAdd(&p.stats[0], (unsigned long long)h);
-      if (m_total) atomicAdd(&p.stats[1], (unsigned long long)m_total);
-      if (rs) atomicAdd(&p.stats[2], (unsigned long long)rs);
-      if (tr2) atomicAdd(&p.stats[4], (unsigned long long)tr2);
+  if (wid == 0) {  // lane w of wave 0 adds wave w's counters
+    const bool in = lane < kResolveWaves;
+    const int h = __builtin_amdgcn_readlane(
+        (int)wave_inclusive_sum(in ? (uint32_t)scr[kScrStats + lane] : 0u), 63);
+    const int rs = __builtin_amdgcn_readlane(
+        (int)wave_inclusive_sum(in ? (uint32_t)scr[kScrStats + 16 + lane] : 0u), 63);
+    const int tr2 = __builtin_amdgcn_readlane(
+        (int)wave_inclusive_sum(in ? (uint32_t)scr[kScrStats + 32 + lane] : 0u), 63);
+    if (lane == 0) {
+      p.plan_cnt[b] = m_total;
+      p.clk[r] = c;
+      if (p.stats) {
+        if (h) atomicAdd(&p.stats[0], (unsigned long long)h);
+        if (m_total) atomicAdd(&p.stats[1], (unsigned long long)m_total);
+        if (rs) atomicAdd(&p.stats[2], (unsigned long long)rs);
+        if (tr2) atomicAdd(&p.stats[4], (unsigned long long)tr2);
+      }
     }
   }
   if (copy_trips && lane == 0 && p.stats) atomicAdd(&p.stats[4], (unsigned long long)copy_trips);
