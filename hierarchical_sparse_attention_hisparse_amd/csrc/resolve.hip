@@ -63,6 +63,20 @@ __device__ inline void load_run(const int32_t* base, int (&v)[N]) {
   }
 }
 
+// N consecutive int32 to `base` as 16-byte (or N*4-byte) vector stores.
+template <int N>
+__device__ inline void store_run(int32_t* base, const int (&v)[N]) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      ((i32x4*)base)[q] = i32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  } else if constexpr (N == 2) {
+    *(i32x2*)base = i32x2{v[0], v[1]};
+  } else {
+    base[0] = v[0];
+  }
+}
+
 __device__ inline int lane_prefix(uint64_t m) {  // popcount of m below this lane
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -390,8 +404,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     const int i = i0 + j;
     const int s = e_hit[i];
     if (s != INT_MAX) {
-      outb[i] = rowbase + s;
-      lru[s] = c;
+      outb[i] = rowbase + s;  // the slot's owner refreshes its stamp
       ++n_hit;
     } else {
       missbits |= 1u << j;
@@ -458,6 +471,9 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     key[j] = ((uint64_t)(sr[j] >= 0 ? 1u : 0u) << 32) | (uint64_t)((uint32_t)lr[j] ^ 0x80000000u);
     if (s0 + j < S && !(hitm & (1u << j))) cand |= 1u << j;
   }
+  int vr[SPT];  // rank of this slot among the victims, or -1
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) vr[j] = -1;
   int need = m_total, vbase = 0;
 #pragma unroll 1
   for (int round = 0; round < kVictimRounds && need > 0; ++round) {
@@ -476,7 +492,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     for (int j = 0; j < SPT; ++j) {
       if ((cand & (1u << j)) && key[j] == kmin) {
         if (pos < need) {
-          victim[vbase + pos] = s0 + j;
+          vr[j] = vbase + pos;
           cand &= ~(1u << j);
         }
         ++pos;
@@ -515,6 +531,21 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       const int s = (int)(s_sort[j] & 0xFFFFull);
       victim[vbase + j] = s < S ? s : S - 1;  // always < S: candidates >= misses
     }
+    // The sorted victims' ranks by slot, in the (now dead) sort region.
+    int32_t* vrank = (int32_t*)s_sort;
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if (s0 + j < S) vrank[s0 + j] = -1;
+    lds_barrier();
+    for (int j = tid; j < need; j += kResolveThreads) vrank[victim[vbase + j]] = vbase + j;
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if (cand & (1u << j)) {
+        const int v = vrank[s0 + j];
+        if (v >= 0) vr[j] = v;
+      }
   }
   if (!COPY) {
     int mp = mpos0;
@@ -524,26 +555,47 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   }
   lds_barrier();
 
-  // Step 5: the j-th miss takes the j-th victim; emit the compact plan.  The
-  // fused copy keeps its own copy of the plan in the (now dead) table region.
+  // Step 5: the victim of rank j takes the j-th miss: its owner sets token
+  // and row ID and writes one entry of the compact plan.  The fused copy keeps
+  // its own copy of the plan in the (now dead) table region.  Then every
+  // thread writes its slot run back once: stamps of hit and victim slots,
+  // tokens of victim slots (vector stores, not one scattered store per slot).
   int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
   int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
   int64_t* f_src = (int64_t*)(smem + L.off_hash);          // [k]
   int32_t* f_dst = (int32_t*)(smem + L.off_hash + 8 * (size_t)k);  // [k]
-  for (int j = tid; j < m_total; j += kResolveThreads) {
-    const int i = m_entry[j];
-    const int s = victim[j];
-    const int t = e_tok[i];
-    st[s] = t;
-    lru[s] = c;
-    const int row = rowbase + s;
+  unsigned vict = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    if (vr[j] < 0) continue;
+    vict |= 1u << j;
+    const int v = vr[j];
+    const int i = m_entry[v];
+    sr[j] = e_tok[i];
+    const int row = rowbase + s0 + j;
     outb[i] = row;
-    const int64_t h = m_h[j];  // -1 for a row outside [0, 2^31)
-    psrc[j] = h;
-    pdst[j] = row;
+    const int64_t h = m_h[v];  // -1 for a row outside [0, 2^31)
+    psrc[v] = h;
+    pdst[v] = row;
     if (COPY) {
-      f_src[j] = h;
-      f_dst[j] = row;
+      f_src[v] = h;
+      f_dst[v] = row;
+    }
+  }
+  const unsigned touched = hitm | vict;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if (touched & (1u << j)) lr[j] = c;
+  if constexpr (VEC) {
+    if (s0 < S) {
+      if (touched) store_run<SPT>(lru + s0, lr);
+      if (vict) store_run<SPT>(st + s0, sr);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      if (touched & (1u << j)) lru[s0 + j] = c;
+      if (vict & (1u << j)) st[s0 + j] = sr[j];
     }
   }
 
