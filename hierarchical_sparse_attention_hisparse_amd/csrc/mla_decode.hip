@@ -124,10 +124,13 @@ __device__ inline void load_part(RawPart& R, const DecodeParams& p, int kk, int 
 __device__ inline void store_half(const RawPart& R, unsigned char* tile, int key, int part, int e,
                                   int h) {
   uint4* row = (uint4*)(tile + key * kRowStrideBytes);  // 16-byte units of bf16
-  const float sc = e == 0 ? R.scale.x : e == 1 ? R.scale.y : e == 2 ? R.scale.z : R.scale.w;
+  // A masked key dequantises zero bytes with a zero scale: exact zeros, even
+  // where the row it was read from holds NaN codes.
+  const float sc = R.valid ? (e == 0 ? R.scale.x : e == 1 ? R.scale.y : e == 2 ? R.scale.z : R.scale.w)
+                           : 0.f;
   const uint32_t m = R.valid ? ~0u : 0u;
-  uint4 v = h == 0 ? dequant8(R.lat[e].x, R.lat[e].y, sc) : dequant8(R.lat[e].z, R.lat[e].w, sc);
-  v.x &= m; v.y &= m; v.z &= m; v.w &= m;
+  const uint4 v = h == 0 ? dequant8(R.lat[e].x & m, R.lat[e].y & m, sc)
+                         : dequant8(R.lat[e].z & m, R.lat[e].w & m, sc);
   row[2 * (part + 8 * e) + h] = v;  // 16 fp8 -> 32 bytes of bf16 at unit 2c, c = part + 8e
 }
 
@@ -301,10 +304,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              xv[ht][kt][e] = ((vw[kt] >> (8 * e)) & 0xFF) ? s[kt][ht][e] * sl2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) {  // raw scores; the scale (> 0) is applied below
+              xv[ht][kt][e] = ((vw[kt] >> (8 * e)) & 0xFF) ? s[kt][ht][e] : -INFINITY;
               lmax[ht] = fmaxf(lmax[ht], xv[ht][kt][e]);
             }
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) lmax[ht] *= sl2;
         const bool up0 = lmax[0] > m_run[0] + kMaxExcessLog2;
         const bool up1 = lmax[1] > m_run[1] + kMaxExcessLog2;
         if (__ballot(up0 || up1)) {  // first valid block of a head, or an overflow
@@ -337,10 +342,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float xx = xv[ht][kt][e];
-              // v_exp_f32 without denormal range reduction: results below
-              // 2^-126 flush to zero, negligible against the reference's 1
-              pv[kt][e] = __builtin_amdgcn_exp2f(fminf(xx - mref, kMaxExcessLog2));
+              // x * sl2 - ref in one fma.  v_exp_f32 without denormal range
+              // reduction: results below 2^-126 flush to zero, negligible
+              // against the reference's 1
+              pv[kt][e] = __builtin_amdgcn_exp2f(fminf(fmaf(xv[ht][kt][e], sl2, -mref), kMaxExcessLog2));
               ps += pv[kt][e];
             }
           l_run[ht] += ps;
