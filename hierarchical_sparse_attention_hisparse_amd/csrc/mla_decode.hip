@@ -55,7 +55,8 @@ constexpr int kLatSteps = kLat / 32;              // 16 k-steps over the latent
 constexpr int kQKAhead = 2;                       // LDS reads this many MFMA steps ahead
 constexpr int kTiles = 3;                         // K/V tiles in flight (read, PV, written)
 constexpr size_t kOffFlags = kTiles * (size_t)kTileBytes;
-constexpr size_t kOffOvf = kOffFlags + 128;       // int: a score exceeded its reference by > 2^64
+// per tile: 32 float biases, 0 for a valid key and -inf for a masked one
+constexpr size_t kOffOvf = kOffFlags + kTiles * 32 * sizeof(float);  // int: a score exceeded its reference by > 2^64
 constexpr size_t kOffQRope = kOffOvf + 16;        // [128 heads][72 bf16] rope part of Q
 constexpr int kHeadTiles = kHeadsPerGroup / 16;    // 8
 constexpr int kDimTilesPerWave = kLat / 16 / kDecWaves;  // 8: O dims 128w..128w+127
@@ -140,19 +141,19 @@ __device__ inline void store_chunk(const RawPart& R, unsigned char* tile, int ke
 }
 
 // The rope chunk and the key's validity flag.
-__device__ inline void store_tail(const RawPart& R, unsigned char* tile, uint8_t* vflag, int key,
+__device__ inline void store_tail(const RawPart& R, unsigned char* tile, float* vbias, int key,
                                   int part) {
   uint4* row = (uint4*)(tile + key * kRowStrideBytes);
   const uint32_t m = R.valid ? ~0u : 0u;
   row[kLat / 8 + part] = make_uint4(R.rope.x & m, R.rope.y & m, R.rope.z & m, R.rope.w & m);
-  if (part == 0) vflag[key] = R.valid ? 1 : 0;
+  if (part == 0) vbias[key] = R.valid ? 0.f : -INFINITY;
 }
 
-__device__ inline void store_part(const RawPart& R, unsigned char* tile, uint8_t* vflag, int key,
+__device__ inline void store_part(const RawPart& R, unsigned char* tile, float* vbias, int key,
                                   int part) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_chunk(R, tile, key, part, e);
-  store_tail(R, tile, vflag, key, part);
+  store_tail(R, tile, vbias, key, part);
 }
 
 __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams p) {
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
   const int blk0 = sp * per;
   const int nblk = max(0, min(nb, blk0 + per) - blk0);
   const int32_t* locb = p.locs + (int64_t)b * p.k;
-  uint8_t* vflags = smem + kOffFlags;
+  float* vbiases = (float*)(smem + kOffFlags);
   // First head of this wave.  Waves past the last head compute on clamped
   // queries and their partials are never read: keeping every wave on the same
   // path keeps the accumulators in registers.
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
       load_part(R, p, blk0 * kKB + key, loc_at(p, locb, blk0 * kKB + key), part);
       const int loc1 = loc_at(p, locb, min(blk0 + 1, last) * kKB + key);
       loc_n = loc_at(p, locb, min(blk0 + 2, last) * kKB + key);
-      store_part(R, smem, vflags, key, part);
+      store_part(R, smem, vbiases, key, part);
       load_part(R, p, (blk0 + 1) * kKB + key, loc1, part);
     }
     __syncthreads();
@@ -239,12 +240,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
     for (int i = 0; i < nblk; ++i) {
       const int tnext = tcur == kTiles - 1 ? 0 : tcur + 1;
       const unsigned char* tile = smem + tcur * kTileBytes;
-      const uint8_t* vf = vflags + 32 * tcur;
+      const float* vb = vbiases + 32 * tcur;
       // Block i+1 goes into the third buffer, last read by block i-2's PV,
       // which every wave finished before the previous barrier (past the end
       // of the split it is written and never read).
       unsigned char* ntile = smem + tnext * kTileBytes;
-      uint8_t* nvf = vflags + 32 * tnext;
+      float* nvb = vbiases + 32 * tnext;
       bf16x8 pb[2];
       {
         // S^T = K Q^T: 2 key tiles x 2 head tiles, K fragments shared by both head tiles.
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
                 __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then VALU
               }
             }
-            if (c == 16) store_tail(R, ntile, nvf, key, part);
+            if (c == 16) store_tail(R, ntile, nvb, key, part);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
         loc_n = loc_at(p, locb, min(blk0 + i + 3, nb - 1) * kKB + key);
         // Softmax for head hw+16ht+r16 over the lane's 8 keys (4g..4g+3 and
         // 16+4g..16+4g+3), against the head's reference m_run.
-        const uint32_t vw[2] = {*(const uint32_t*)(vf + 4 * g), *(const uint32_t*)(vf + 16 + 4 * g)};
+        const f32x4 vbk[2] = {*(const f32x4*)(vb + 4 * g), *(const f32x4*)(vb + 16 + 4 * g)};
         float xv[2][2][4];
         float lmax[2] = {-INFINITY, -INFINITY};
 #pragma unroll
@@ -304,8 +305,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {  // raw scores; the scale (> 0) is applied below
-              xv[ht][kt][e] = ((vw[kt] >> (8 * e)) & 0xFF) ? s[kt][ht][e] : -INFINITY;
+            for (int e = 0; e < 4; ++e) {  // raw scores (masked keys -inf); the scale (> 0) is applied below
+              xv[ht][kt][e] = s[kt][ht][e] + vbk[kt][e];
               lmax[ht] = fmaxf(lmax[ht], xv[ht][kt][e]);
             }
 #pragma unroll
