@@ -345,8 +345,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
             for (int e = 0; e < 4; ++e) {
               // x * sl2 - ref in one fma.  v_exp_f32 without denormal range
               // reduction: results below 2^-126 flush to zero, negligible
-              // against the reference's 1
-              pv[kt][e] = __builtin_amdgcn_exp2f(fminf(fmaf(xv[ht][kt][e], sl2, -mref), kMaxExcessLog2));
+              // against the reference's 1.  No clamp: a score more than 64
+              // above its reference has set the overflow flag, and the second
+              // pass recomputes O and l from zero, so a huge or infinite P of
+              // this pass is never used.
+              pv[kt][e] = __builtin_amdgcn_exp2f(fmaf(xv[ht][kt][e], sl2, -mref));
               ps += pv[kt][e];
             }
           l_run[ht] += ps;
