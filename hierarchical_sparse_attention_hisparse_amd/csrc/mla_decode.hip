@@ -16,8 +16,8 @@
 // block's score loop.  With three tiles and two P buffers, the one barrier
 // per block (after P is published) also orders every tile reuse.  Each wavefront
 // computes the scores of its own 32 heads, so every K fragment read from LDS
-// feeds two MFMAs (LDS instruction issue, not bytes, bounds this loop on
-// gfx950), and then O for a quarter of the dims of all 128 heads, so every
+// feeds two MFMAs (instruction issue, not bytes, bounds this loop on gfx950),
+// and then O for a quarter of the dims of all 128 heads, so every
 // transposed V fragment is read once per workgroup and feeds eight MFMAs:
 //  - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q held in registers;
 //  - a softmax against a fixed reference per head: the maximum of the first
@@ -43,8 +43,12 @@ namespace {
 
 constexpr int kKB = 32;                           // keys per block
 constexpr int kLat = 512, kDim = 576;
-constexpr int kTileStride = 584;                  // bf16 per tile row (576 + 8 pad)
-constexpr int kRowStrideBytes = kTileStride * 2;  // 1168: conflict-free b128 / tr16 reads
+// bf16 per tile row (576 + 8 pad).  The bank-conflict counter shows 2-way
+// conflicts at this 1168-byte stride on the b128 K reads and the tr16 V reads
+// (1184 bytes is conflict-free on both), but the kernel measures no faster
+// at 1184: LDS is not what bounds it.
+constexpr int kTileStride = 584;
+constexpr int kRowStrideBytes = kTileStride * 2;
 constexpr int kTileBytes = kKB * kRowStrideBytes;
 constexpr int kDecWaves = 4;
 constexpr int kHeadsPerWave = 32;

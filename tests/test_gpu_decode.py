@@ -127,6 +127,30 @@ def test_decode_repeated_calls_on_one_pool():
         hb.free()
 
 
+def test_decode_masked_keys_ignore_what_row_zero_holds():
+    """Masked and out-of-range entries are read from row 0 and dequantised
+    with a zero scale; with row 0 all 0xFF bytes (NaN latent codes, a NaN
+    scale, NaN rope values) the output must still match the oracle, which
+    skips those entries."""
+    print("[decode] masked keys over a NaN row 0", flush=True)
+    B, H, k, rows = 3, 64, 200, 700
+    dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 12, gen_device="cuda")
+    dev[0].fill_(0xFF)
+    rng = np.random.default_rng(12)
+    locs = rng.integers(1, rows, size=(B, k)).astype(np.int32)
+    locs[:, ::5] = -1
+    locs[2, 1::9] = rows + 3
+    q = make_queries(B, H, seed=12, device="cuda")
+    got = _run_decode(dev, locs, q, H, k)
+    assert np.all(np.isfinite(got))
+    ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16), locs,
+                                   dev.cpu().numpy(), float(np.float32(SCALE)))
+    err = _normwise(got, ref)
+    print("[decode] masked keys max normwise error %.3g" % err.max(), flush=True)
+    assert err.max() <= TOL
+
+
 def test_decode_all_invalid_gives_zero():
     dev = torch.empty((64, 656), dtype=torch.uint8, device="cuda")
     fill_host_rows_mla(dev, 3, gen_device="cuda")
