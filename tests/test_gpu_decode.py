@@ -96,8 +96,8 @@ def test_decode_score_far_above_the_first_block():
 
 
 def test_decode_repeated_calls_on_one_pool():
-    """Calls of different shapes on one pool: the split workspace grows and
-    the arrival counters are left at zero for the next call."""
+    """Calls of different shapes on one pool: the split workspace grows, and
+    a later call with fewer splits still reads only its own partials."""
     print("[decode] repeated calls", flush=True)
     rows = 1200
     dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
