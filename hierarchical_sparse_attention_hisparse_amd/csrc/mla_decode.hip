@@ -56,7 +56,7 @@ constexpr int kHeadsPerGroup = kDecWaves * kHeadsPerWave;  // 128
 constexpr float kMaxExcessLog2 = 64.f;            // largest score above a head's reference (log2)
 constexpr int kQRopeStrideBytes = 144;            // 64 bf16 + 16 pad: conflict-free b128 reads
 constexpr int kLatSteps = kLat / 32;              // 16 k-steps over the latent
-constexpr int kQKAhead = 2;                       // LDS reads this many MFMA steps ahead
+constexpr int kQKAhead = 3;                       // LDS reads this many MFMA steps ahead (measured: 1 and 2 slower, 4 no faster)
 constexpr int kTiles = 3;                         // K/V tiles in flight (read, PV, written)
 constexpr size_t kOffFlags = kTiles * (size_t)kTileBytes;
 // per tile: 32 float biases, 0 for a valid key and -inf for a masked one
