@@ -109,3 +109,76 @@ def test_decode_replayed_from_a_graph():
     finally:
         hs.hisparse_destroy_pool(pool)
         hb.free()
+
+
+def test_overlapped_layers_replayed_from_a_graph():
+    """Plan plus the overlapped per-layer copy and decode (two pool streams
+    forked from the caller's stream by events and joined back) captured once
+    and replayed: each replay equals the eager sequential order bit for bit
+    (row IDs, state, counters, device pools, every layer's output)."""
+    print("[graph] overlapped layers", flush=True)
+    B, L, H = 9, 3, 32
+    scale = 1.0 / math.sqrt(192.0)
+    w = synth("ovlgraph", 91, R=B, S=256, k=128, steps=5, n0=[3000 + 700 * b for b in range(B)],
+              L=L, grow=1, keep=80, recent=16, recent_window=64)
+    bufs = make_host_pools(w, kind="mla")
+    seq = Pair(w, bufs, with_oracle=False)
+    ovl = Pair(w, bufs, with_oracle=False)
+    try:
+        qs = [make_queries(w.B, H, seed=20 + l, device="cuda") for l in range(L)]
+        outs_s = [torch.empty((w.B, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        outs_o = [torch.empty((w.B, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        topk_s = ovl.topk[0].clone()
+        seq_s = ovl.seq[0].clone()
+
+        def sequential(step):
+            seq.pre_step_writes(step)
+            hs.hisparse_resolve_plan(seq.pool, None, w.B, w.k, seq.req_idx, seq.topk[step],
+                                     seq.seq[step], seq.locs, seq.bt, seq.st, seq.lru, seq.clk,
+                                     seq.out, seq.stats)
+            hs.hisparse_gather_copy(seq.pool, None, w.B, 0, L, seq.stats)
+            for l in range(L):
+                hs.hisparse_sparse_mla_decode(seq.pool, None, w.B, H, w.k, l, qs[l], seq.out, scale,
+                                              outs_s[l])
+
+        def overlapped():
+            hs.hisparse_resolve_plan(ovl.pool, None, w.B, w.k, ovl.req_idx, topk_s, seq_s, ovl.locs,
+                                     ovl.bt, ovl.st, ovl.lru, ovl.clk, ovl.out, ovl.stats)
+            hs.hisparse_decode_layers_overlapped(ovl.pool, None, w.B, H, w.k, qs, ovl.out, scale,
+                                                 outs_o, ovl.stats)
+
+        def compare(step):
+            torch.cuda.synchronize()
+            assert torch.equal(seq.out, ovl.out), "row IDs, step %d" % step
+            for a, b in ((seq.st, ovl.st), (seq.lru, ovl.lru), (seq.clk, ovl.clk),
+                         (seq.stats, ovl.stats)):
+                assert torch.equal(a, b), "state, step %d" % step
+            for l in range(L):
+                assert torch.equal(seq.dev_pools[l], ovl.dev_pools[l]), "pool %d, step %d" % (l, step)
+                assert torch.equal(outs_s[l], outs_o[l]), "output of layer %d, step %d" % (l, step)
+
+        # step 0 eagerly on both sides: it also creates the pool's streams,
+        # events and decode workspace, which capture cannot
+        sequential(0)
+        ovl.pre_step_writes(0)
+        overlapped()
+        compare(0)
+
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            overlapped()
+        torch.cuda.synchronize()
+
+        for step in range(1, w.steps):
+            sequential(step)
+            ovl.pre_step_writes(step)
+            topk_s.copy_(ovl.topk[step])
+            seq_s.copy_(ovl.seq[step])
+            graph.replay()
+            compare(step)
+            print("[graph] overlapped replay of step %d equals the sequential order" % step, flush=True)
+    finally:
+        seq.close()
+        ovl.close()
