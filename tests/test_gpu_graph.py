@@ -182,3 +182,97 @@ def test_overlapped_layers_replayed_from_a_graph():
     finally:
         seq.close()
         ovl.close()
+
+
+def test_steps_and_maintenance_replayed_from_a_graph():
+    """Two verification steps, a row mirror, invalidation by token range and
+    by host rows, captured once and replayed for five decode steps on one
+    pool; an identical pool runs the same calls eagerly.  Every replay must
+    leave both bit-identical: row IDs, state, counters, device pools and the
+    mirrored host rows."""
+    print("[graph] verification steps and maintenance", flush=True)
+    Q, D, k, L, B = 2, 5, 64, 2, 9
+    w = synth("stepsgraph", 93, R=B + 1, S=(Q + 1) * k, k=k, steps=Q * D,
+              n0=[3000 + 500 * b for b in range(B)], L=L, grow=1, keep=k // 2, recent=k // 4,
+              recent_window=2 * k)
+    eager = Pair(w, make_host_pools(w), with_oracle=False, max_steps=Q)
+    graphed = Pair(w, make_host_pools(w), with_oracle=False, max_steps=Q)
+    rng = np.random.default_rng(93)
+    try:
+        r0 = int(w.req_idx[0])
+        dev = torch.device("cuda")
+        # per pair: static inputs and outputs of the captured calls
+        st_in = {}
+        for name, p in (("eager", eager), ("graphed", graphed)):
+            st_in[name] = dict(
+                topk=torch.empty((Q, w.B, w.k), dtype=torch.int32, device=dev),
+                seq=torch.empty((Q, w.B), dtype=torch.int32, device=dev),
+                out=torch.empty((Q, w.B, w.k), dtype=torch.int32, device=dev),
+                mir_d=torch.empty(8, dtype=torch.int32, device=dev),
+                mir_h=torch.empty(8, dtype=torch.int64, device=dev),
+                inv_lo=torch.empty(w.B, dtype=torch.int32, device=dev),
+                inv_hi=torch.empty(w.B, dtype=torch.int32, device=dev),
+                inv_rows=torch.empty(16, dtype=torch.int64, device=dev))
+
+        def calls(p, s):
+            hs.hisparse_resolve_steps(p.pool, None, Q, w.B, w.k, p.req_idx, s["topk"], s["seq"],
+                                      p.locs, p.bt, p.st, p.lru, p.clk, s["out"], p.stats)
+            hs.hisparse_mirror_rows(p.pool, None, s["mir_d"], s["mir_h"], stats=p.stats)
+            hs.hisparse_invalidate_tokens(p.pool, None, p.req_idx, s["inv_lo"], s["inv_hi"], p.st,
+                                          p.lru, p.stats)
+            hs.hisparse_invalidate_host_rows(p.pool, None, s["inv_rows"], p.locs, p.st, p.lru)
+
+        def inputs(d):
+            sl = slice(d * Q, (d + 1) * Q)
+            n_last = w.seq_lens[d * Q + Q - 1]
+            mir_d = np.array([r0 * w.S + (d * 8 + j) % w.S for j in range(8)], np.int32)
+            mir_h = np.array([w.host_pool_rows - 1 - (d * 8 + j) for j in range(8)], np.int64)
+            inv_lo = np.maximum(n_last - 40, 0).astype(np.int32)
+            inv_hi = np.maximum(n_last - 30, 0).astype(np.int32)
+            inv_rows = np.sort(rng.choice(w.host_pool_rows - 64, size=16, replace=False)).astype(np.int64)
+            for name, p in (("eager", eager), ("graphed", graphed)):
+                for q in range(Q):
+                    p.pre_step_writes(d * Q + q)
+                s = st_in[name]
+                s["topk"].copy_(p.topk[sl])
+                s["seq"].copy_(p.seq[sl])
+                s["mir_d"].copy_(torch.from_numpy(mir_d))
+                s["mir_h"].copy_(torch.from_numpy(mir_h))
+                s["inv_lo"].copy_(torch.from_numpy(inv_lo))
+                s["inv_hi"].copy_(torch.from_numpy(inv_hi))
+                s["inv_rows"].copy_(torch.from_numpy(inv_rows))
+
+        def compare(d):
+            torch.cuda.synchronize()
+            a, b = st_in["eager"], st_in["graphed"]
+            assert torch.equal(a["out"], b["out"]), "row IDs, decode step %d" % d
+            for x, y, what in ((eager.st, graphed.st, "slot_tokens"), (eager.lru, graphed.lru, "lru"),
+                               (eager.clk, graphed.clk, "clock"), (eager.stats, graphed.stats, "stats")):
+                assert torch.equal(x, y), "%s, decode step %d" % (what, d)
+            for l in range(L):
+                assert torch.equal(eager.dev_pools[l], graphed.dev_pools[l]), "pool %d" % l
+                tail = slice(w.host_pool_rows - 64, w.host_pool_rows)
+                assert np.array_equal(eager.host_np[l][tail], graphed.host_np[l][tail]), "host %d" % l
+
+        inputs(0)
+        calls(eager, st_in["eager"])
+        calls(graphed, st_in["graphed"])   # eager warm-up of the graphed pool
+        compare(0)
+
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            calls(graphed, st_in["graphed"])
+        torch.cuda.synchronize()
+
+        for d in range(1, D):
+            inputs(d)
+            calls(eager, st_in["eager"])
+            graph.replay()
+            compare(d)
+            print("[graph] decode step %d: replay equals the eager calls" % d, flush=True)
+        assert int(graphed.stats[1].item()) > 0
+    finally:
+        eager.close()
+        graphed.close()
