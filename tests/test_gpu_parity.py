@@ -203,3 +203,36 @@ def test_host_side_errors():
         torch.cuda.synchronize()
     finally:
         pair.close()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_duplicate_positions_are_safe(mode):
+    """Distinct positions per row are a caller precondition; with repeats the
+    results are unspecified (the oracle and the kernel may place a repeat
+    differently), but the kernel must finish, emit only row IDs inside the
+    device pool (or -1), copy only into hot rows, and keep working on the
+    in-contract steps that follow."""
+    print("[duplicates %s]" % mode, flush=True)
+    w = synth("dups", 27, R=10, S=128, k=48, steps=6, n0=[3000, 2500, 900, 4000, 5000, 1200, 3500,
+                                                          2800, 700, 6000], keep=30)
+    pair = Pair(w, make_host_pools(w), with_oracle=False, mode=mode)
+    try:
+        rng = np.random.default_rng(27)
+        for step in range(w.steps):
+            if step in (1, 3):   # repeat some valid positions inside their rows
+                tk = w.top_k[step].copy()
+                for b in range(w.B):
+                    src = rng.choice(w.k, size=6, replace=False)
+                    dst = rng.choice(w.k, size=6, replace=False)
+                    tk[b, dst] = tk[b, src]
+                pair.topk[step].copy_(torch.from_numpy(tk))
+            pair.gpu_step(step)
+            torch.cuda.synchronize()
+            out = pair.out.cpu().numpy()
+            assert ((out == -1) | ((out >= 0) & (out < w.dev_pool_rows))).all(), "step %d" % step
+            st = pair.st.cpu().numpy()
+            assert ((st >= -1) & (st < w.max_seq_len)).all()
+        stats = pair.stats.cpu().numpy()
+        assert stats[0] > 0 and stats[1] > 0 and stats[4] == 0
+    finally:
+        pair.close()
