@@ -67,6 +67,33 @@ def test_decode_small_vs_oracle(B, H, k):
     assert err.max() <= TOL
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_shapes_vs_oracle(seed):
+    """Seeded random shapes: batch 1-4, 16-144 heads (one or two head groups,
+    a partial second group), 1-300 keys, masked and out-of-range entries at a
+    random rate, sometimes a row with nothing to attend to."""
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 5))
+    H = int(rng.choice([16, 32, 48, 64, 128, 144]))
+    k = int(rng.integers(1, 301))
+    rows = k + int(rng.integers(16, 400))
+    print("[decode random %d] B=%d H=%d k=%d rows=%d" % (seed, B, H, k, rows), flush=True)
+    dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 600 + seed, gen_device="cuda")
+    locs = rng.integers(0, rows, size=(B, k)).astype(np.int32)
+    locs[rng.random((B, k)) < rng.uniform(0.0, 0.5)] = -1
+    locs[rng.random((B, k)) < 0.03] = rows + 5
+    if B > 1 and rng.random() < 0.5:
+        locs[int(rng.integers(0, B)), :] = -1
+    q = make_queries(B, H, seed=700 + seed, device="cuda")
+    got = _run_decode(dev, locs, q, H, k)
+    ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16), locs,
+                                   dev.cpu().numpy(), float(np.float32(SCALE)))
+    err = _normwise(got, ref)
+    print("[decode random %d] max normwise error %.3g" % (seed, err.max()), flush=True)
+    assert err.max() <= TOL
+
+
 def test_decode_score_far_above_the_first_block():
     """One key in a late block scores far above everything in the first block
     (a query aligned with that key's K vector), so the kernel's second pass
