@@ -105,3 +105,44 @@ def test_resolve_steps_bounds():
         torch.cuda.synchronize()
     finally:
         pair.close()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_resolve_steps_random_vs_oracle(seed):
+    """Seeded random verification-step calls: 1-4 steps per call, random k,
+    batch and layers, hot slots between steps * k and (steps + 2) * k; every
+    position's row IDs, and the state after each call, bit-exact against the
+    same positions as consecutive oracle calls."""
+    rng = np.random.default_rng(800 + seed)
+    Q = int(rng.integers(1, 5))
+    D = int(rng.integers(2, 4))
+    k = int(rng.integers(1, 97))
+    B = int(rng.integers(1, 12))
+    L = int(rng.integers(1, 4))
+    S = Q * k + int(rng.integers(0, 2 * k + 1))
+    n0 = [int(v) for v in rng.integers(1, 8 * S, size=B)]
+    keep = int(rng.integers(0, k + 1))
+    print("[steps random %d] Q=%d D=%d k=%d S=%d B=%d L=%d" % (seed, Q, D, k, S, B, L), flush=True)
+    w = synth("mtprand%d" % seed, 900 + seed, R=B + 1, S=S, k=k, steps=Q * D, n0=n0, L=L, grow=1,
+              keep=keep)
+    pair = Pair(w, make_host_pools(w), max_steps=Q)
+    try:
+        out = torch.empty((Q, w.B, w.k), dtype=torch.int32, device="cuda")
+        for d in range(D):
+            sl = slice(d * Q, (d + 1) * Q)
+            for q in range(Q):
+                pair.pre_step_writes(d * Q + q)
+            hs.hisparse_resolve_steps(pair.pool, None, Q, w.B, w.k, pair.req_idx,
+                                      pair.topk[sl].contiguous(), pair.seq[sl].contiguous(),
+                                      pair.locs, pair.bt, pair.st, pair.lru, pair.clk, out,
+                                      pair.stats)
+            o_outs = [pair.oracle_step(d * Q + q, *pair.writes_of(d * Q + q)) for q in range(Q)]
+            torch.cuda.synchronize()
+            g = out.cpu().numpy()
+            for q in range(Q):
+                assert np.array_equal(g[q], o_outs[q]), "decode step %d position %d" % (d, q)
+            pair.out.copy_(out[Q - 1])
+            pair.compare_step(d * Q + Q - 1, o_outs[Q - 1])
+        pair.compare_pools()
+    finally:
+        pair.close()
