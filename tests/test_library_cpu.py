@@ -66,3 +66,37 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
+    """include/hisparse.h compiles as strict C99 and as C++17; a C program
+    links libhisparse.so and gets a status code and message back from a call
+    whose arguments are refused on the host (no GPU needed)."""
+    import shutil
+    import subprocess
+    import hierarchical_sparse_attention_hisparse_amd as hs
+    from hierarchical_sparse_attention_hisparse_amd.build import build_library
+    if shutil.which("gcc") is None or shutil.which("g++") is None:
+        pytest.skip("no host C/C++ compiler")
+    if not os.path.exists(hs.library_path()):
+        build_library(force=True)
+    inc = os.path.join(ROOT, "include")
+    libdir = os.path.dirname(hs.library_path())
+    src = tmp_path / "use_abi.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "hisparse.h"\n'
+        "int main(void) {\n"
+        "  hisparse_pool* pool = NULL;\n"
+        "  int rc = hisparse_init_pool(NULL, NULL, NULL, NULL, 0, &pool);\n"
+        '  printf("%d %s\\n", rc, hisparse_last_error());\n'
+        "  return rc == HISPARSE_EINVAL && pool == NULL ? 0 : 1;\n"
+        "}\n")
+    exe = tmp_path / "use_abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", inc,
+                    str(src), "-L", libdir, "-lhisparse", "-Wl,-rpath," + libdir, "-o", str(exe)],
+                   check=True)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++", "-I", inc,
+                    str(src)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.startswith("-1 ") and "NULL" in res.stdout
