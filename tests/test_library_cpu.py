@@ -100,3 +100,77 @@ def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.startswith("-1 ") and "NULL" in res.stdout
+
+
+def _init_rc(cfg_kwargs, device_pool_rows=None, layer0=None):
+    """hisparse_init_pool through the C ABI.  The pool arrays are NULL unless
+    `layer0` = (host pointer, host rows, device pointer) is given; those
+    pointers are only checked on the host, never dereferenced."""
+    import hierarchical_sparse_attention_hisparse_amd as hs
+    from hierarchical_sparse_attention_hisparse_amd._binding import _Config
+    base = dict(max_requests=4, slots=256, max_top_k=64, max_batch=4, row_bytes=656, num_layers=1,
+                page_size=0, max_steps=1, resident_pages=0, max_seq_len=1024)
+    base.update(cfg_kwargs)
+    cfg = _Config(**base)
+    lib = hs.load_library()
+    out = ctypes.c_void_p(1)
+    rows = base["max_requests"] * base["slots"] if device_pool_rows is None else device_pool_rows
+    if layer0 is not None:
+        hp = (ctypes.c_void_p * 1)(layer0[0])
+        hr = (ctypes.c_int64 * 1)(layer0[1])
+        dp = (ctypes.c_void_p * 1)(layer0[2])
+        rc = lib.hisparse_init_pool(ctypes.byref(cfg), hp, hr, dp, ctypes.c_int64(rows),
+                                    ctypes.byref(out))
+    else:
+        rc = lib.hisparse_init_pool(ctypes.byref(cfg), None, None, None, ctypes.c_int64(rows),
+                                    ctypes.byref(out))
+    return rc, hs.hisparse_last_error(), out.value
+
+
+@pytest.mark.parametrize("bad", [
+    dict(max_requests=0), dict(slots=0), dict(slots=16385), dict(max_top_k=0),
+    dict(max_top_k=257), dict(max_batch=0), dict(max_batch=65536), dict(row_bytes=650),
+    dict(row_bytes=0), dict(num_layers=0), dict(page_size=-1), dict(max_steps=-1),
+    dict(resident_pages=3), dict(max_seq_len=0), dict(max_seq_len=2 ** 31)])
+def test_init_rejects_bad_configurations_on_the_host(bad):
+    """Every configuration check of hisparse_init_pool runs before any device
+    call: each bad field is refused with EINVAL, a message, and no pool."""
+    rc, msg, out = _init_rc(bad)
+    assert rc == -1, (bad, rc, msg)
+    assert msg and out is None
+
+
+def test_init_rejects_a_device_pool_too_small_for_the_hot_rows():
+    rc, msg, out = _init_rc(dict(max_requests=4, slots=256), device_pool_rows=4 * 256 - 1)
+    assert rc == -1 and "device_pool_rows" in msg and out is None
+    rc, msg, _ = _init_rc(dict(max_requests=4, slots=256, page_size=16, resident_pages=10),
+                          device_pool_rows=4 * 256 + 159)
+    assert rc == -1 and "device_pool_rows" in msg
+
+
+@pytest.mark.parametrize("S,k,fits", [(4096, 2048, True), (4096, 4096, True), (8192, 4096, True),
+                                      (16384, 1976, True), (16384, 1984, False),
+                                      (16384, 4096, False)])
+def test_lds_budget_limits_stated_in_the_header(S, k, fits):
+    """The header's limits on max_top_k per slot count: shapes within them
+    pass every configuration check (the call then stops at the NULL pool
+    arrays), shapes beyond them are refused with EUNSUPPORTED and the LDS
+    bytes they would need."""
+    rc, msg, out = _init_rc(dict(max_requests=2, slots=S, max_top_k=k, max_seq_len=1 << 20))
+    if fits:
+        assert rc == -1 and "pool arrays are NULL" in msg, (S, k, rc, msg)
+    else:
+        assert rc == -4 and "LDS" in msg, (S, k, rc, msg)
+    assert out is None
+
+
+@pytest.mark.parametrize("layer0,what", [((0x10000, 2 ** 31, 0x20000), "host_pool_rows"),
+                                          ((0x10008, 16, 0x20000), "host_pools"),
+                                          (((0), 16, 0x20000), "host_pools"),
+                                          ((0x10000, 16, 0), "device_pools"),
+                                          ((0x10000, 16, 0x20004), "device_pools")])
+def test_init_rejects_bad_pool_arrays_on_the_host(layer0, what):
+    """Per-layer pool checks (row count below 2^31, non-NULL 16-byte-aligned
+    pointers) also run before any device call."""
+    rc, msg, out = _init_rc({}, layer0=layer0)
+    assert rc == -1 and what in msg and out is None, (layer0, rc, msg)
