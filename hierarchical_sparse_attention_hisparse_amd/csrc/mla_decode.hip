@@ -28,7 +28,8 @@
 //    by more than that, the workgroup runs a second pass over its keys with a
 //    reference that the first pass has shown to be high enough;
 //  - P^T fragments taken straight from the S^T accumulator layout (keys
-//    permuted consistently) are exchanged through LDS (one more barrier);
+//    permuted consistently) are exchanged through LDS (the block's one
+//    barrier);
 //  - O^T += V^T P^T with the V^T fragments read from the same row-major tile
 //    with the LDS transpose load (ds_read_b64_tr_b16).
 // Each workgroup writes its O normalised by its own denominator (bf16) with
