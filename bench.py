@@ -36,10 +36,12 @@ HOST_LINK_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 DECODE_HEADS = 128
 ROW_BYTES = 656
+_CSRC = "hierarchical_sparse_attention_hisparse_amd/csrc/"
+# each profiled kernel's source with the headers it includes
 KERNEL_SOURCES = {
-    "gather_copy": "hierarchical_sparse_attention_hisparse_amd/csrc/gather.hip",
-    "resolve": "hierarchical_sparse_attention_hisparse_amd/csrc/resolve.hip",
-    "resolve_fused": "hierarchical_sparse_attention_hisparse_amd/csrc/resolve.hip",
+    "gather_copy": [_CSRC + "gather.hip", _CSRC + "common.h", _CSRC + "kernels.h"],
+    "resolve": [_CSRC + "resolve.hip", _CSRC + "common.h", _CSRC + "kernels.h"],
+    "resolve_fused": [_CSRC + "resolve.hip", _CSRC + "common.h", _CSRC + "kernels.h"],
 }
 
 
@@ -47,9 +49,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def src_hash(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(rels):
+    h = hashlib.sha256()
+    for rel in ([rels] if isinstance(rels, str) else rels):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel):

@@ -34,7 +34,8 @@ constexpr int kCopyThreads = 256;
 #endif
 constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
 constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
-constexpr int kCopyRowsInFlight = 4;  // rows per wavefront per iteration of the fused copy
+constexpr int kCopyRowsInFlight = 3;  // rows per wavefront per iteration of the fused copy (measured: 1, 2, 4 and 8 slower)
+constexpr int kNarrowCopyRowsInFlight = 4;  // the same for the narrow copy beside the decode (3 is slower there)
 constexpr int kNarrowCopyThreads = 1024;  // narrow copy (beside decode): threads per workgroup
 #ifndef HISPARSE_NARROW_COPY_GROUPS
 #define HISPARSE_NARROW_COPY_GROUPS 32

@@ -49,13 +49,13 @@ typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memo
 
 // Narrow form, for a copy that runs beside another kernel: gridDim.x
 // workgroups of 1024 threads walk the batch rows (grid stride), each
-// wavefront copying kCopyRowsInFlight rows per iteration, so the copy holds
+// wavefront copying kNarrowCopyRowsInFlight rows per iteration, so the copy holds
 // few CUs while keeping enough rows in flight for the host link.  Row
 // indices are wave-uniform; the bytes and tripwires are those of the wide
 // form.
 __global__ __launch_bounds__(kNarrowCopyThreads) void gather_copy_narrow_kernel(CopyParams p, int batch) {
   constexpr int W = kNarrowCopyThreads / kWave;
-  constexpr int RIF = kCopyRowsInFlight;
+  constexpr int RIF = kNarrowCopyRowsInFlight;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int l = p.layer_begin + blockIdx.y;
