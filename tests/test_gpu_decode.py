@@ -42,10 +42,14 @@ def _run_decode(dev_pool, locs_np, q, heads, max_top_k):
         hb.free()
 
 
-# Key splits per row at these shapes: 3, 2, 2, 10, 4, 16 and 8, so the split
-# combine runs at each of its unrolled widths (2, 4, 8, 16).
+# Key splits per row at these shapes: 3, 2, 2, 10, 4, 16, 8, 16, 1 and 1, so
+# the split combine runs at each of its unrolled widths (2, 4, 8, 16).  The
+# last three: the largest top-k the resolver takes (4096 keys, 16 splits of 8
+# blocks), one split because the batch alone fills the CUs (160 rows), and
+# one split because a single ragged block holds every key.
 @pytest.mark.parametrize("B,H,k", [(5, 32, 77), (3, 16, 33), (2, 48, 64), (4, 128, 300),
-                                   (3, 256, 100), (1, 128, 2048), (32, 64, 256)])
+                                   (3, 256, 100), (1, 128, 2048), (32, 64, 256), (2, 128, 4096),
+                                   (160, 128, 96), (1, 16, 20)])
 def test_decode_small_vs_oracle(B, H, k):
     print("[decode] B=%d H=%d k=%d" % (B, H, k), flush=True)
     rows = max(900, k + 64)
