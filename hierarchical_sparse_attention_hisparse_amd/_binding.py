@@ -173,6 +173,9 @@ def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False):
         raise ValueError("%s is required" % name)
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a device (cuda) tensor" % name)
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on cuda:%d, not on the current device cuda:%d"
+                         % (name, t.device.index, torch.cuda.current_device()))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
@@ -183,10 +186,13 @@ def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False):
 
 
 class _Pool:
-    def __init__(self, handle: int, cfg: PoolConfig, device_pool_rows: int):
+    def __init__(self, handle: int, cfg: PoolConfig, device_pool_rows: int, keep=()):
         self.handle = handle
         self.cfg = cfg
         self.device_pool_rows = device_pool_rows
+        # The library keeps raw pointers to the device pools and host buffers:
+        # hold them for as long as the pool lives.
+        self._keep = tuple(keep)
 
 
 def hisparse_init_pool(config: PoolConfig, host_pools, host_pool_rows, device_pools,
@@ -214,13 +220,14 @@ def hisparse_init_pool(config: PoolConfig, host_pools, host_pool_rows, device_po
                                                  ctypes.cast(dp, ctypes.c_void_p),
                                                  device_pool_rows, ctypes.byref(out)),
               "hisparse_init_pool")
-    return _Pool(int(out.value), config, device_pool_rows)
+    return _Pool(int(out.value), config, device_pool_rows, keep=list(device_pools) + list(host_pools))
 
 
 def hisparse_destroy_pool(pool: _Pool):
     if pool is not None and pool.handle:
         load_library().hisparse_destroy_pool(ctypes.c_void_p(pool.handle))
         pool.handle = 0
+        pool._keep = ()
 
 
 def _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cache_locs,

@@ -205,6 +205,26 @@ def test_host_side_errors():
         pair.close()
 
 
+def test_pool_holds_its_buffers():
+    """The library keeps raw pointers to the device pools and host buffers,
+    so the binding's pool object keeps them alive until it is destroyed: a
+    caller that drops its own references must not leave the kernels writing
+    into memory handed out again."""
+    import gc
+    import weakref
+    hb = hs.HostBuffer(656 * 64)
+    dev = torch.zeros((64, 656), dtype=torch.uint8, device="cuda")
+    refs = (weakref.ref(hb), weakref.ref(dev))
+    cfg = hs.PoolConfig(max_requests=1, slots=64, max_top_k=16, max_batch=1, max_seq_len=64)
+    pool = hs.hisparse_init_pool(cfg, [hb], [64], [dev], 64)
+    del hb, dev
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    hs.hisparse_destroy_pool(pool)
+    gc.collect()
+    assert all(r() is None for r in refs)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_duplicate_positions_are_safe(mode):
     """Distinct positions per row are a caller precondition; with repeats the
