@@ -29,10 +29,6 @@ struct hisparse_pool {
   uint4* zero_row;              // row_bytes of zeros (source of out-of-range host rows)
   void* dec_ws;                 // decode split partials, grown on demand
   size_t dec_ws_bytes;
-  // overlapped decode, created on first use: per-layer ready events plus
-  // entry / exit events, and two streams
-  hipEvent_t* layer_ready;      // [L + 3]
-  hipStream_t ovl_copy, ovl_compute;
   // host copies
   unsigned char** dev_ptrs;     // [L]
   unsigned char** host_ptrs;    // [L] device-mapped host pool pointers
@@ -152,7 +148,7 @@ int copy_chunks_for(int batch) {
 }
 
 int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t lb, int32_t le,
-                uint64_t* stats, int32_t slice = 0, bool narrow = false) {
+                uint64_t* stats, int32_t slice = 0) {
   CopyParams c;
   c.host_pools = pool->d_host_ptrs;
   c.dev_pools = pool->d_dev_ptrs;
@@ -166,8 +162,7 @@ int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   c.units = pool->cfg.row_bytes / 16;
   c.chunks = copy_chunks_for(batch);
   c.layer_begin = lb;
-  hipError_t e = narrow ? launch_gather_copy_narrow(c, batch, le - lb, kNarrowCopyGroups, stream)
-                        : launch_gather_copy(c, batch, le - lb, stream);
+  hipError_t e = launch_gather_copy(c, batch, le - lb, stream);
   if (e != hipSuccess) return hip_fail(e, "gather copy kernel launch");
   return HISPARSE_OK;
 }
@@ -341,12 +336,6 @@ void hisparse_destroy_pool(hisparse_pool* pool) {
   if (!pool) return;
   if (pool->plan_src) (void)hipFree(pool->plan_src);
   if (pool->dec_ws) (void)hipFree(pool->dec_ws);
-  if (pool->layer_ready) {
-    for (int l = 0; l < pool->cfg.num_layers + 3; ++l) (void)hipEventDestroy(pool->layer_ready[l]);
-    free(pool->layer_ready);
-  }
-  if (pool->ovl_copy) (void)hipStreamDestroy(pool->ovl_copy);
-  if (pool->ovl_compute) (void)hipStreamDestroy(pool->ovl_compute);
   free(pool->dev_ptrs);
   free(pool->host_ptrs);
   free(pool->host_rows);
@@ -560,10 +549,10 @@ int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t cou
   return ok();
 }
 
-static int decode_one(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,
-                               int32_t top_k, int32_t layer, const void* q_bf16,
-                               const int32_t* device_buffer_locs, float softmax_scale,
-                               void* out_bf16) {
+// Argument checks of one decode call (nothing is enqueued).
+static int decode_check(hisparse_pool* pool, int32_t batch, int32_t heads, int32_t top_k,
+                        int32_t layer, const void* q_bf16, const int32_t* device_buffer_locs,
+                        void* out_bf16) {
   if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
   if (batch < 0) return fail(HISPARSE_EINVAL, "batch %d < 0", batch);
   if (heads <= 0 || heads % 16 != 0)
@@ -575,13 +564,21 @@ static int decode_one(hisparse_pool* pool, void* stream, int32_t batch, int32_t 
   if (pool->cfg.row_bytes < 656)
     return fail(HISPARSE_EUNSUPPORTED, "row_bytes %d is smaller than the 656-byte sparse-MLA row",
                 pool->cfg.row_bytes);
-  if (batch == 0) return ok();
+  if (batch == 0) return HISPARSE_OK;
   if (!q_bf16 || !out_bf16 || (top_k > 0 && !device_buffer_locs))
     return fail(HISPARSE_EINVAL, "q_bf16, out_bf16 and device_buffer_locs must not be NULL");
   if (!aligned(q_bf16, 16) || !aligned(out_bf16, 8) || !aligned(device_buffer_locs, 4))
     return fail(HISPARSE_EINVAL, "q_bf16 must be 16-byte, out_bf16 8-byte and locs 4-byte aligned");
-  int rc = check_device(pool);
-  if (rc != HISPARSE_OK) return rc;
+  return HISPARSE_OK;
+}
+
+// One decode call on checked arguments (batch > 0).  With copy_layer >= 0,
+// the same launch also copies that layer's misses (plan slice 0) in
+// workgroups past the decode's own.
+static int decode_launch(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t heads,
+                         int32_t top_k, int32_t layer, const void* q_bf16,
+                         const int32_t* device_buffer_locs, float softmax_scale, void* out_bf16,
+                         int32_t copy_layer, uint64_t* stats) {
   const int splits = decode_splits(batch, heads, top_k);
   const size_t need = decode_workspace_bytes(batch, heads, splits);
   if (need > pool->dec_ws_bytes) {  // grow the split workspace (synchronises the device)
@@ -603,7 +600,7 @@ static int decode_one(hisparse_pool* pool, void* stream, int32_t batch, int32_t 
   }
   // bf16 partial O, then fp32 (reference, denominator) per (row, group, split, head)
   const size_t entries = need / (512 * sizeof(uint16_t) + 2 * sizeof(float));
-  DecodeParams d;
+  DecodeParams d = {};
   d.splits = splits;
   d.part_o = (uint16_t*)pool->dec_ws;
   d.part_ml = (float*)(d.part_o + entries * 512);
@@ -617,26 +614,33 @@ static int decode_one(hisparse_pool* pool, void* stream, int32_t batch, int32_t 
   d.q = (const uint16_t*)q_bf16;
   d.locs = device_buffer_locs;
   d.out = (uint16_t*)out_bf16;
-  hipError_t e = launch_sparse_mla_decode(d, batch, (hipStream_t)stream);
+  if (copy_layer >= 0) {
+    d.copy_host = pool->host_ptrs[copy_layer];
+    d.copy_dev = pool->dev_ptrs[copy_layer];
+    d.copy_host_rows = pool->host_rows[copy_layer];
+    d.plan_src = pool->plan_src;
+    d.plan_dst = pool->plan_dst;
+    d.plan_cnt = pool->plan_cnt;
+    d.plan_stride = pool->cfg.max_top_k;
+    d.units = pool->cfg.row_bytes / 16;
+    d.stats = (unsigned long long*)stats;
+  }
+  hipError_t e = launch_sparse_mla_decode(d, batch, stream);
   if (e != hipSuccess) return hip_fail(e, "sparse-MLA decode kernel launch");
-  return ok();
+  return HISPARSE_OK;
 }
 
 int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch, int32_t heads,
                                int32_t top_k, int32_t layer, const void* q_bf16,
                                const int32_t* device_buffer_locs, float softmax_scale,
                                void* out_bf16) {
-  return decode_one(pool, stream, batch, heads, top_k, layer, q_bf16, device_buffer_locs,
-                    softmax_scale, out_bf16);
-}
-
-// Streams of the overlapped decode: two plain non-blocking streams of the
-// pool, default priority.
-static int make_overlap_streams(hisparse_pool* pool) {
-  hipError_t e = hipStreamCreateWithFlags(&pool->ovl_copy, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&pool->ovl_compute, hipStreamNonBlocking);
-  if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
-  return HISPARSE_OK;
+  int rc = decode_check(pool, batch, heads, top_k, layer, q_bf16, device_buffer_locs, out_bf16);
+  if (rc != HISPARSE_OK) return rc;
+  if (batch == 0) return ok();
+  if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
+  rc = decode_launch(pool, (hipStream_t)stream, batch, heads, top_k, layer, q_bf16,
+                     device_buffer_locs, softmax_scale, out_bf16, -1, nullptr);
+  return rc == HISPARSE_OK ? ok() : rc;
 }
 
 int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t batch,
@@ -649,44 +653,24 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t
     return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
   if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
   if (batch == 0) return ok();
-  int rc = check_device(pool);
-  if (rc != HISPARSE_OK) return rc;
   const int L = pool->cfg.num_layers;
-  if (!pool->ovl_copy && (rc = make_overlap_streams(pool)) != HISPARSE_OK) return rc;
-  if (!pool->layer_ready) {
-    hipEvent_t* ev = (hipEvent_t*)calloc((size_t)L + 3, sizeof(hipEvent_t));
-    if (!ev) return fail(HISPARSE_ENOMEM, "host allocation failed");
-    for (int l = 0; l < L + 3; ++l) {
-      hipError_t e = hipEventCreateWithFlags(&ev[l], hipEventDisableTiming);
-      if (e != hipSuccess) {
-        for (int j = 0; j < l; ++j) (void)hipEventDestroy(ev[j]);
-        free(ev);
-        return hip_fail(e, "hipEventCreateWithFlags");
-      }
-    }
-    pool->layer_ready = ev;
-  }
-  hipStream_t cs = pool->ovl_compute, ps = pool->ovl_copy, us = (hipStream_t)stream;
-  hipEvent_t* ev = pool->layer_ready;
-  // both streams start after the caller's work so far (the plan included)
-  hipError_t e = hipEventRecord(ev[L], us);
-  if (e == hipSuccess) e = hipStreamWaitEvent(ps, ev[L], 0);
-  if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[L], 0);
-  if (e != hipSuccess) return hip_fail(e, "entry event");
+  int rc;
+  for (int l = 0; l < L; ++l)  // every layer's arguments before anything is enqueued
+    if ((rc = decode_check(pool, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
+                           out_bf16[l])) != HISPARSE_OK)
+      return rc;
+  if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
+  // All on the caller's stream, so no cross-stream events: layer 0's copy
+  // alone, then one launch per layer that decodes layer l while its spare
+  // workgroups copy layer l + 1 (each launch reads only rows the one before
+  // it finished copying).
+  hipStream_t us = (hipStream_t)stream;
+  if ((rc = launch_copy(pool, us, batch, 0, 1, stats)) != HISPARSE_OK) return rc;
   for (int l = 0; l < L; ++l) {
-    rc = launch_copy(pool, ps, batch, l, l + 1, stats, 0, true);
-    if (rc != HISPARSE_OK) return rc;
-    e = hipEventRecord(ev[l], ps);
-    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[l], 0);
-    if (e != hipSuccess) return hip_fail(e, "layer event");
-    rc = decode_one(pool, cs, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
-                    softmax_scale, out_bf16[l]);
+    rc = decode_launch(pool, us, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
+                       softmax_scale, out_bf16[l], l + 1 < L ? l + 1 : -1, stats);
     if (rc != HISPARSE_OK) return rc;
   }
-  // the caller's stream continues after the last decode (which follows every copy)
-  e = hipEventRecord(ev[L + 1], cs);
-  if (e == hipSuccess) e = hipStreamWaitEvent(us, ev[L + 1], 0);
-  if (e != hipSuccess) return hip_fail(e, "exit event");
   return ok();
 }
 

@@ -35,12 +35,17 @@ constexpr int kCopyThreads = 256;
 constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
 constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
 constexpr int kCopyRowsInFlight = 3;  // rows per wavefront per iteration of the fused copy (measured: 1, 2, 4 and 8 slower)
-constexpr int kNarrowCopyRowsInFlight = 4;  // the same for the narrow copy beside the decode (3 is slower there)
-constexpr int kNarrowCopyThreads = 1024;  // narrow copy (beside decode): threads per workgroup
-#ifndef HISPARSE_NARROW_COPY_GROUPS
-#define HISPARSE_NARROW_COPY_GROUPS 32
+// The next layer's copy inside a decode launch (pipelined layer loop): rows
+// per wavefront per iteration, and about how many workgroups it adds to the
+// decode's (batch rows x chunks of each row's misses).
+#ifndef HISPARSE_LAYER_COPY_RIF
+#define HISPARSE_LAYER_COPY_RIF 8
 #endif
-constexpr int kNarrowCopyGroups = HISPARSE_NARROW_COPY_GROUPS;  // and workgroups, so decode keeps the other CUs
+constexpr int kLayerCopyRowsInFlight = HISPARSE_LAYER_COPY_RIF;
+#ifndef HISPARSE_LAYER_COPY_GROUPS
+#define HISPARSE_LAYER_COPY_GROUPS 128
+#endif
+constexpr int kLayerCopyGroups = HISPARSE_LAYER_COPY_GROUPS;
 
 // Invalidation by host rows: sets up to this many rows are searched in LDS.
 constexpr int kInvalidateLdsRows = 8192;

@@ -44,72 +44,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_copy_kernel(CopyParams p)
   }
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memory
-
-// Narrow form, for a copy that runs beside another kernel: gridDim.x
-// workgroups of 1024 threads walk the batch rows (grid stride), each
-// wavefront copying kNarrowCopyRowsInFlight rows per iteration, so the copy holds
-// few CUs while keeping enough rows in flight for the host link.  Row
-// indices are wave-uniform; the bytes and tripwires are those of the wide
-// form.
-__global__ __launch_bounds__(kNarrowCopyThreads) void gather_copy_narrow_kernel(CopyParams p, int batch) {
-  constexpr int W = kNarrowCopyThreads / kWave;
-  constexpr int RIF = kNarrowCopyRowsInFlight;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  const int l = p.layer_begin + blockIdx.y;
-  const int U = p.units;
-  const gu4* hp = (const gu4*)p.host_pools[l];
-  gu4* dp = (gu4*)p.dev_pools[l];
-  const int64_t hrows = p.host_rows[l];
-  int trips = 0;
-  for (int b = blockIdx.x; b < batch; b += gridDim.x) {
-    const int m = p.plan_cnt[b];
-    const int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
-    const int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
-    for (int e0 = wv; e0 < m; e0 += W * RIF) {
-      int64_t h[RIF];
-      int32_t d[RIF];
-      bool real[RIF], ok[RIF];
-#pragma unroll
-      for (int q = 0; q < RIF; ++q) {
-        const int e = e0 + q * W;
-        real[q] = e < m;
-        const int eq = real[q] ? e : e0;
-        const int64_t hv = psrc[eq];
-        h[q] = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)hv) |
-               ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(hv >> 32)) << 32);
-        d[q] = __builtin_amdgcn_readfirstlane(pdst[eq]);
-        ok[q] = h[q] >= 0 && h[q] < hrows;
-        trips += (real[q] && !ok[q]) ? 1 : 0;
-      }
-      for (int part = lane; part < U; part += kWave) {
-        u32x4 v[RIF];
-#pragma unroll
-        for (int q = 0; q < RIF; ++q) {
-          v[q] = u32x4{0u, 0u, 0u, 0u};
-          if (real[q] && ok[q]) v[q] = hp[h[q] * U + part];
-        }
-#pragma unroll
-        for (int q = 0; q < RIF; ++q)
-          if (real[q]) dp[(int64_t)d[q] * U + part] = v[q];
-      }
-    }
-  }
-  if (trips && lane == 0 && p.stats) atomicAdd(&p.stats[4], (unsigned long long)trips);
-}
-
 }  // namespace
-
-hipError_t launch_gather_copy_narrow(const CopyParams& p, int batch, int layers, int groups,
-                                     hipStream_t stream) {
-  if (batch <= 0 || layers <= 0) return hipSuccess;
-  const int g = groups < batch ? groups : batch;
-  hipLaunchKernelGGL(gather_copy_narrow_kernel, dim3(g, layers), dim3(kNarrowCopyThreads), 0,
-                     stream, p, batch);
-  return hipGetLastError();
-}
 
 hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream) {
   if (batch <= 0 || layers <= 0) return hipSuccess;

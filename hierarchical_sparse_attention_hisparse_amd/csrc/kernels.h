@@ -68,6 +68,19 @@ struct DecodeParams {
   int32_t splits;        // key splits per (batch row, 128-head group)
   uint16_t* part_o;      // bf16 [batch][groups][splits][128][512] O of a split / its denominator
   float* part_ml;        // [batch][groups][splits][128][2] reference (log2), denominator
+  // Optional copy of another layer's misses (plan slice 0) by workgroups
+  // launched past the decode's own: copy_dev == nullptr for none.
+  const unsigned char* copy_host;  // device-mapped host pool of the copied layer
+  unsigned char* copy_dev;         // its device pool
+  int64_t copy_host_rows;
+  const int64_t* plan_src;
+  const int32_t* plan_dst;
+  const int32_t* plan_cnt;
+  unsigned long long* stats;       // copy tripwires go to stats[4]; may be null
+  int32_t plan_stride;
+  int32_t units;                   // row_bytes / 16
+  int32_t decode_blocks;           // set by the launch
+  int32_t copy_chunks;             // set by the launch: workgroups per batch row of the copy
 };
 
 struct MirrorParams {
@@ -100,9 +113,6 @@ struct InvalidateParams {
 hipError_t prepare_resolve(size_t lds_bytes);
 hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream);
 hipError_t launch_gather_copy(const CopyParams& p, int batch, int layers, hipStream_t stream);
-// The same copy on at most `groups` workgroups of 1024 threads.
-hipError_t launch_gather_copy_narrow(const CopyParams& p, int batch, int layers, int groups,
-                                     hipStream_t stream);
 hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream);
 hipError_t prepare_sparse_mla_decode();
 size_t decode_lds_bytes();

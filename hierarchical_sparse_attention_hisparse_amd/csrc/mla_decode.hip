@@ -161,8 +161,71 @@ __device__ inline void store_part(const RawPart& R, unsigned char* tile, float* 
   store_tail(R, tile, vbias, key, part);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memory
+
+// The copy role of workgroup g of the batch * copy_chunks launched past the
+// decode's own: chunk c of batch row b (g = b * copy_chunks + c) takes every
+// (4 * copy_chunks)-th miss of that row, from the copied layer's host pool
+// into its device pool, one wavefront per 656-byte row (lane l carries
+// 16-byte unit l) and kLayerCopyRowsInFlight rows in flight per wavefront.
+// The first of these workgroups run on the CUs the decode leaves free, the
+// rest as decode workgroups finish.  A host row outside the pool writes zeros
+// and counts a tripwire, as in the separate copy kernel.
+__device__ inline void layer_copy(const DecodeParams& p, int g) {
+  constexpr int RIF = kLayerCopyRowsInFlight;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int U = p.units;
+  const gu4* hp = (const gu4*)p.copy_host;
+  gu4* dp = (gu4*)p.copy_dev;
+  const int b = g / p.copy_chunks, c = g - b * p.copy_chunks;
+  const int stride = kDecWaves * p.copy_chunks;
+  int trips = 0;
+  {
+    const int m = p.plan_cnt[b];
+    const int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
+    const int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
+    for (int e0 = c * kDecWaves + wv; e0 < m; e0 += stride * RIF) {
+      int64_t h[RIF];
+      int32_t d[RIF];
+      bool real[RIF], ok[RIF];
+#pragma unroll
+      for (int q = 0; q < RIF; ++q) {
+        const int e = e0 + q * stride;
+        real[q] = e < m;
+        const int eq = real[q] ? e : e0;
+        const int64_t hv = psrc[eq];
+        h[q] = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)hv) |
+               ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(hv >> 32)) << 32);
+        d[q] = __builtin_amdgcn_readfirstlane(pdst[eq]);
+        ok[q] = h[q] >= 0 && h[q] < p.copy_host_rows;
+        trips += (real[q] && !ok[q]) ? 1 : 0;
+      }
+      for (int part = lane; part < U; part += 64) {
+        u32x4 v[RIF];
+#pragma unroll
+        for (int q = 0; q < RIF; ++q) {
+          v[q] = u32x4{0u, 0u, 0u, 0u};
+          if (real[q] && ok[q]) v[q] = hp[h[q] * U + part];
+        }
+#pragma unroll
+        for (int q = 0; q < RIF; ++q)
+          if (real[q]) dp[(int64_t)d[q] * U + part] = v[q];
+      }
+    }
+  }
+  if (trips && lane == 0 && p.stats) atomicAdd(&p.stats[4], (unsigned long long)trips);
+}
+
 __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  // Workgroups past the decode's copy another layer's misses (uniform per
+  // workgroup, before any barrier).
+  if ((int)blockIdx.x >= p.decode_blocks) {
+    layer_copy(p, (int)blockIdx.x - p.decode_blocks);
+    return;
+  }
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
   const int NS = p.splits;
   int x = blockIdx.x;
@@ -530,11 +593,18 @@ hipError_t prepare_sparse_mla_decode() {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds_bytes());
 }
 
-hipError_t launch_sparse_mla_decode(const DecodeParams& p, int batch, hipStream_t stream) {
+hipError_t launch_sparse_mla_decode(const DecodeParams& dp, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
+  DecodeParams p = dp;
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  const int grid = batch * HG * p.splits;
-  hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(grid), dim3(256), decode_lds_bytes(), stream, p);
+  p.decode_blocks = batch * HG * p.splits;
+  // A copy beside the decode: each of its workgroups holds a whole CU, so
+  // the first take the CUs the decode leaves free and the rest follow the
+  // decode workgroups as they finish.
+  p.copy_chunks = p.copy_dev ? (kLayerCopyGroups + batch - 1) / batch : 0;
+  const int cg = batch * p.copy_chunks;
+  hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(p.decode_blocks + cg), dim3(256), decode_lds_bytes(),
+                     stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per_row = p.heads * (kLat / 8);

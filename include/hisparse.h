@@ -328,16 +328,17 @@ int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t cou
 /*
  * hisparse_decode_layers_overlapped -- the miss copy and the decode of every
  * layer, pipelined: after a plan (hisparse_resolve_plan, or slice 0 of
- * hisparse_resolve_steps) enqueued on `stream`, layer l's copy runs on a
- * copy stream and is followed by its own ready event; a compute stream
- * waits for that event and runs layer l's decode, so the copy of layer l+1
- * overlaps the attention of layer l.  This is the layer-group pipelining of
- * "vLLM Hybrid HiSparse 源码实现分析" section 6 (each group is submitted when
- * ready and synchronised by its last layer's event) on the swap-in side.
- * The two streams belong to the pool (created on first use, default
- * priority); `stream` waits for both at the end.  Results are those of hisparse_gather_copy of all layers followed
- * by hisparse_sparse_mla_decode of each layer l with q_bf16[l] and
- * out_bf16[l] (host arrays of L device pointers).  Errors: as those calls.
+ * hisparse_resolve_steps) enqueued on `stream`, layer 0's misses are copied,
+ * then each layer's decode runs in one launch with the copy of the next
+ * layer's misses, so the copy of layer l+1 overlaps the attention of layer
+ * l.  This is the layer-group pipelining of "vLLM Hybrid HiSparse 源码实现分析"
+ * section 6 (each group is submitted when ready) on the swap-in side.
+ * Everything is enqueued on `stream` alone, in stream order (no other
+ * streams or events).  Results are those of hisparse_gather_copy of all
+ * layers followed by hisparse_sparse_mla_decode of each layer l with
+ * q_bf16[l] and out_bf16[l] (host arrays of L device pointers); stats[4]
+ * counts the copy's tripwires.  Every layer's arguments are checked before
+ * anything is enqueued.  Errors: as those calls.
  */
 int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t batch,
                                       int32_t heads, int32_t top_k, const void* const* q_bf16,
