@@ -399,8 +399,8 @@ def next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, warmup, ste
         "layers": L, "heads": DECODE_HEADS, "steps": n_ovl,
         "sequential_ms_per_step": seq_ms, "overlapped_ms_per_step": ovl_ms,
         "speedup": seq_ms / ovl_ms,
-        "note": "plan, then per layer: miss copy and decode on the pool's two streams vs "
-                "the same kernels in order on one stream",
+        "note": "plan, then layer 0's copy and one launch per layer that decodes it while "
+                "copying the next layer, vs the copy of all layers then each decode, in order",
     }
     return res
 
