@@ -572,15 +572,21 @@ static int decode_check(hisparse_pool* pool, int32_t batch, int32_t heads, int32
   return HISPARSE_OK;
 }
 
-// One decode call on checked arguments (batch > 0).  With copy_layer >= 0,
-// the same launch also copies that layer's misses (plan slice 0) in
-// workgroups past the decode's own.
+// One decode call on checked arguments (batch > 0), for the layer pipeline
+// optionally: with copy_layer >= 0 the same launch also copies that layer's
+// misses (plan slice 0) in workgroups past the decode's own; its split
+// partials go to half `half` of a two-half workspace; comb_out != nullptr
+// combines the other half (the previous call of the same shape) into it in
+// workgroups after the copy's; defer leaves this call's combine to the next
+// launch.  A plain call (half -1) uses a one-half workspace.
 static int decode_launch(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t heads,
                          int32_t top_k, int32_t layer, const void* q_bf16,
                          const int32_t* device_buffer_locs, float softmax_scale, void* out_bf16,
-                         int32_t copy_layer, uint64_t* stats) {
+                         int32_t copy_layer = -1, uint64_t* stats = nullptr, int half = -1,
+                         void* comb_out = nullptr, bool defer = false) {
   const int splits = decode_splits(batch, heads, top_k);
-  const size_t need = decode_workspace_bytes(batch, heads, splits);
+  const size_t one = decode_workspace_bytes(batch, heads, splits);
+  const size_t need = half >= 0 ? 2 * one : one;
   if (need > pool->dec_ws_bytes) {  // grow the split workspace (synchronises the device)
     if (pool->dec_ws) {
       hipError_t fe = hipFree(pool->dec_ws);
@@ -598,12 +604,22 @@ static int decode_launch(hisparse_pool* pool, hipStream_t stream, int32_t batch,
     pool->dec_ws = w;
     pool->dec_ws_bytes = need;
   }
-  // bf16 partial O, then fp32 (reference, denominator) per (row, group, split, head)
-  const size_t entries = need / (512 * sizeof(uint16_t) + 2 * sizeof(float));
+  // each half: bf16 partial O, then fp32 (reference, denominator) per
+  // (row, group, split, head)
+  const size_t entries = one / (512 * sizeof(uint16_t) + 2 * sizeof(float));
+  unsigned char* ws = (unsigned char*)pool->dec_ws;
+  unsigned char* mine = ws + (half > 0 ? one : 0);
   DecodeParams d = {};
   d.splits = splits;
-  d.part_o = (uint16_t*)pool->dec_ws;
+  d.part_o = (uint16_t*)mine;
   d.part_ml = (float*)(d.part_o + entries * 512);
+  if (comb_out) {
+    unsigned char* other = ws + (half > 0 ? 0 : one);
+    d.comb_part_o = (const uint16_t*)other;
+    d.comb_part_ml = (const float*)(d.comb_part_o + entries * 512);
+    d.comb_out = (uint16_t*)comb_out;
+  }
+  d.defer_combine = defer ? 1 : 0;
   d.pool = pool->dev_ptrs[layer];
   d.pool_rows = pool->device_pool_rows;
   d.row_bytes = pool->cfg.row_bytes;
@@ -639,7 +655,7 @@ int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream, int32_t batch,
   if (batch == 0) return ok();
   if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
   rc = decode_launch(pool, (hipStream_t)stream, batch, heads, top_k, layer, q_bf16,
-                     device_buffer_locs, softmax_scale, out_bf16, -1, nullptr);
+                     device_buffer_locs, softmax_scale, out_bf16);
   return rc == HISPARSE_OK ? ok() : rc;
 }
 
@@ -662,13 +678,17 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t
   if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
   // All on the caller's stream, so no cross-stream events: layer 0's copy
   // alone, then one launch per layer that decodes layer l while its spare
-  // workgroups copy layer l + 1 (each launch reads only rows the one before
-  // it finished copying).
+  // workgroups copy layer l + 1 and combine layer l - 1's splits (each
+  // launch reads only rows the one before it finished copying, and the
+  // split partials of layers l and l - 1 sit in the two halves of the
+  // workspace); the last layer's combine follows as its own kernel.
   hipStream_t us = (hipStream_t)stream;
   if ((rc = launch_copy(pool, us, batch, 0, 1, stats)) != HISPARSE_OK) return rc;
   for (int l = 0; l < L; ++l) {
+    const bool last = l + 1 == L;
     rc = decode_launch(pool, us, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
-                       softmax_scale, out_bf16[l], l + 1 < L ? l + 1 : -1, stats);
+                       softmax_scale, out_bf16[l], last ? -1 : l + 1, stats, l & 1,
+                       l > 0 ? out_bf16[l - 1] : nullptr, !last);
     if (rc != HISPARSE_OK) return rc;
   }
   return ok();

@@ -46,6 +46,7 @@ constexpr int kLayerCopyRowsInFlight = HISPARSE_LAYER_COPY_RIF;
 #define HISPARSE_LAYER_COPY_GROUPS 128
 #endif
 constexpr int kLayerCopyGroups = HISPARSE_LAYER_COPY_GROUPS;
+constexpr int kLayerCombineGroups = 128;  // workgroups of the previous layer's combine in the same launch
 
 // Invalidation by host rows: sets up to this many rows are searched in LDS.
 constexpr int kInvalidateLdsRows = 8192;

@@ -81,6 +81,14 @@ struct DecodeParams {
   int32_t units;                   // row_bytes / 16
   int32_t decode_blocks;           // set by the launch
   int32_t copy_chunks;             // set by the launch: workgroups per batch row of the copy
+  // Optional combine of a previous call's splits (same batch, heads and
+  // splits) by workgroups launched after the copy's: comb_out == nullptr for
+  // none.  defer_combine: leave this call's own combine to a later launch.
+  const uint16_t* comb_part_o;
+  const float* comb_part_ml;
+  uint16_t* comb_out;
+  int32_t comb_groups;             // set by the launch
+  int32_t defer_combine;
 };
 
 struct MirrorParams {

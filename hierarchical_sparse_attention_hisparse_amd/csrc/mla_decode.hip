@@ -218,13 +218,97 @@ __device__ inline void layer_copy(const DecodeParams& p, int g) {
   if (trips && lane == 0 && p.stats) atomicAdd(&p.stats[4], (unsigned long long)trips);
 }
 
+// Combine the splits of every (batch row, head): O = sum_j w_j l_j O_j /
+// sum_j w_j l_j with w_j = 2^(m_j - max m), O_j the normalised partials.
+// One thread per 8 output dims: thread tid of block bx of batch row b, so
+// every index is 32-bit shifts and masks.  All splits' (m, l) pairs and
+// partial rows (at most NSMAX) are loaded before any is combined.
+template <int NSMAX>
+__device__ inline void combine_rows(const uint16_t* part_o, const float* part_ml, uint16_t* out,
+                                    int heads, int splits, int bx, int b, int tid) {
+  const int t = bx * 256 + tid;  // over heads x (kLat / 8)
+  const int h = t / (kLat / 8), q = t % (kLat / 8);
+  if (h >= heads) return;
+  const int HG = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const int hg = h / kHeadsPerGroup, hl = h % kHeadsPerGroup;
+  const int NS = splits;
+  const int64_t e0 = ((int64_t)(b * HG + hg) * NS) * kHeadsPerGroup + hl;
+  f32x2 ml[NSMAX];
+  uint4 v[NSMAX];
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NSMAX; ++j) {
+    ml[j] = f32x2{-INFINITY, 0.f};
+    v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < NS) {
+      const int64_t e = e0 + (int64_t)j * kHeadsPerGroup;
+      ml[j] = *(const f32x2*)(part_ml + 2 * e);
+      v[j] = *(const uint4*)(part_o + e * kLat + 8 * q);
+    }
+    M = fmaxf(M, ml[j].x);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < NSMAX; ++j) {
+      if (j < NS && ml[j].x != -INFINITY) {
+        const float wl = exp2f(ml[j].x - M) * ml[j].y;
+        L += wl;
+        const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += wl * __uint_as_float(wd[k] << 16);
+          acc[2 * k + 1] += wl * __uint_as_float(wd[k] & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint4 w;
+  w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *(uint4*)(out + ((int64_t)b * heads + h) * kLat + 8 * q) = w;
+}
+
+// The combine role of workgroup g of the comb_groups launched after the
+// copy's: the combine of the previous layer's splits (the same arithmetic
+// as the combine kernel), block by block over (batch row, block of 256
+// threads).
+__device__ inline void combine_role(const DecodeParams& p, int g) {
+  const int xb = (p.heads * (kLat / 8) + 255) / 256;
+  const int total = xb * p.batch;
+  for (int cb = g; cb < total; cb += p.comb_groups) {
+    const int b = cb / xb, bx = cb - b * xb;
+    if (p.splits <= 2)
+      combine_rows<2>(p.comb_part_o, p.comb_part_ml, p.comb_out, p.heads, p.splits, bx, b, threadIdx.x);
+    else if (p.splits <= 4)
+      combine_rows<4>(p.comb_part_o, p.comb_part_ml, p.comb_out, p.heads, p.splits, bx, b, threadIdx.x);
+    else if (p.splits <= 8)
+      combine_rows<8>(p.comb_part_o, p.comb_part_ml, p.comb_out, p.heads, p.splits, bx, b, threadIdx.x);
+    else
+      combine_rows<16>(p.comb_part_o, p.comb_part_ml, p.comb_out, p.heads, p.splits, bx, b, threadIdx.x);
+  }
+}
+
+// ROLES: the instance of the layer pipeline, whose workgroups past the
+// decode's copy another layer's misses, then combine the previous layer's
+// splits (uniform per workgroup, before any barrier).  A separate instance,
+// because the extra code costs the plain decode scalar-register spills.
+template <bool ROLES>
 __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // Workgroups past the decode's copy another layer's misses (uniform per
-  // workgroup, before any barrier).
-  if ((int)blockIdx.x >= p.decode_blocks) {
-    layer_copy(p, (int)blockIdx.x - p.decode_blocks);
-    return;
+  if constexpr (ROLES) {
+    if ((int)blockIdx.x >= p.decode_blocks) {
+      const int x = (int)blockIdx.x - p.decode_blocks, ncopy = p.batch * p.copy_chunks;
+      if (x < ncopy)
+        layer_copy(p, x);
+      else
+        combine_role(p, x - ncopy);
+      return;
+    }
   }
   const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
   const int NS = p.splits;
@@ -514,59 +598,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_decode_kernel(DecodeParams 
   }
 }
 
-// Combine the splits of every (batch row, head): O = sum_j w_j l_j O_j /
-// sum_j w_j l_j with w_j = 2^(m_j - max m), O_j the normalised partials.
-// One thread per 8 output dims; grid.y is the batch row, so every index is
-// 32-bit shifts and masks.  All splits' (m, l) pairs and partial rows (at
-// most NSMAX) are loaded before any is combined.
+
+// The combine kernel: grid (blocks of 256 threads per batch row, batch).
 template <int NSMAX>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-  const int b = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;  // over heads x (kLat / 8)
-  const int h = t / (kLat / 8), q = t % (kLat / 8);
-  if (h >= p.heads) return;
-  const int HG = (p.heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  const int hg = h / kHeadsPerGroup, hl = h % kHeadsPerGroup;
-  const int NS = p.splits;
-  const int64_t e0 = ((int64_t)(b * HG + hg) * NS) * kHeadsPerGroup + hl;
-  f32x2 ml[NSMAX];
-  uint4 v[NSMAX];
-  float M = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NSMAX; ++j) {
-    ml[j] = f32x2{-INFINITY, 0.f};
-    v[j] = make_uint4(0u, 0u, 0u, 0u);
-    if (j < NS) {
-      const int64_t e = e0 + (int64_t)j * kHeadsPerGroup;
-      ml[j] = *(const f32x2*)(p.part_ml + 2 * e);
-      v[j] = *(const uint4*)(p.part_o + e * kLat + 8 * q);
-    }
-    M = fmaxf(M, ml[j].x);
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < NSMAX; ++j) {
-      if (j < NS && ml[j].x != -INFINITY) {
-        const float wl = exp2f(ml[j].x - M) * ml[j].y;
-        L += wl;
-        const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[2 * k] += wl * __uint_as_float(wd[k] << 16);
-          acc[2 * k + 1] += wl * __uint_as_float(wd[k] & 0xFFFF0000u);
-        }
-      }
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint4 w;
-  w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-  w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  *(uint4*)(p.out + ((int64_t)b * p.heads + h) * kLat + 8 * q) = w;
+  combine_rows<NSMAX>(p.part_o, p.part_ml, p.out, p.heads, p.splits, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 }  // namespace
@@ -589,7 +625,10 @@ size_t decode_workspace_bytes(int batch, int heads, int splits) {
 }
 
 hipError_t prepare_sparse_mla_decode() {
-  return hipFuncSetAttribute((const void*)sparse_mla_decode_kernel,
+  hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_decode_kernel<false>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds_bytes());
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)sparse_mla_decode_kernel<true>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds_bytes());
 }
 
@@ -603,10 +642,16 @@ hipError_t launch_sparse_mla_decode(const DecodeParams& dp, int batch, hipStream
   // decode workgroups as they finish.
   p.copy_chunks = p.copy_dev ? (kLayerCopyGroups + batch - 1) / batch : 0;
   const int cg = batch * p.copy_chunks;
-  hipLaunchKernelGGL(sparse_mla_decode_kernel, dim3(p.decode_blocks + cg), dim3(256), decode_lds_bytes(),
-                     stream, p);
+  // The previous layer's combine, after the copy's workgroups.
+  p.comb_groups = p.comb_out ? kLayerCombineGroups : 0;
+  if (cg + p.comb_groups > 0)
+    hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, dim3(p.decode_blocks + cg + p.comb_groups),
+                       dim3(256), decode_lds_bytes(), stream, p);
+  else
+    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, dim3(p.decode_blocks), dim3(256),
+                       decode_lds_bytes(), stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.defer_combine) return e;
   const int per_row = p.heads * (kLat / 8);
   const dim3 cgrid((unsigned)((per_row + 255) / 256), (unsigned)batch);
   static_assert(kMaxDecodeSplits <= 16, "combine instances");

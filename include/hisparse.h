@@ -330,8 +330,8 @@ int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t cou
  * layer, pipelined: after a plan (hisparse_resolve_plan, or slice 0 of
  * hisparse_resolve_steps) enqueued on `stream`, layer 0's misses are copied,
  * then each layer's decode runs in one launch with the copy of the next
- * layer's misses, so the copy of layer l+1 overlaps the attention of layer
- * l.  This is the layer-group pipelining of "vLLM Hybrid HiSparse 源码实现分析"
+ * layer's misses and the split combine of the previous layer, so the copy
+ * of layer l+1 overlaps the attention of layer l.  This is the layer-group pipelining of "vLLM Hybrid HiSparse 源码实现分析"
  * section 6 (each group is submitted when ready) on the swap-in side.
  * Everything is enqueued on `stream` alone, in stream order (no other
  * streams or events).  Results are those of hisparse_gather_copy of all
