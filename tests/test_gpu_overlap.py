@@ -16,14 +16,20 @@ pytestmark = pytest.mark.gpu
 SCALE = 1.0 / math.sqrt(192.0)
 
 
-@pytest.mark.parametrize("B,corrupt", [(4, False), (9, False), (9, True)])
-def test_overlapped_layers_match_sequential(B, corrupt):
+# Layer counts 1 (no copy or combine beside any decode), 2, 3 and 5 (the
+# split partials alternate between two workspace halves, so odd and even
+# counts end on different halves); 260 batch rows of one key split each make
+# the decode alone fill the CUs, so the copy and combine workgroups of each
+# launch run after it.
+@pytest.mark.parametrize("B,L,corrupt", [(4, 3, False), (9, 3, False), (9, 3, True), (5, 1, False),
+                                         (6, 2, True), (7, 5, False), (260, 2, False)])
+def test_overlapped_layers_match_sequential(B, L, corrupt):
     """With `corrupt`, some host rows are out of range (negative or past the
-    pool), so the narrow copy's zero fill and tripwire count are compared
+    pool), so the layer copy's zero fill and tripwire count are compared
     too."""
-    print("[overlap] B=%d corrupt=%s" % (B, corrupt), flush=True)
-    L, H = 3, 32
-    n0 = [3000 + 700 * b for b in range(B)]
+    print("[overlap] B=%d L=%d corrupt=%s" % (B, L, corrupt), flush=True)
+    H = 32
+    n0 = [3000 + 700 * b for b in range(B)] if B <= 64 else [600 + 7 * b for b in range(B)]
     w = synth("ovl", 70 + B, R=B, S=256, k=128, steps=3, n0=n0, L=L, grow=1, keep=80, recent=16,
               recent_window=64)
     if corrupt:   # every request is past S, so admission copies no host rows
