@@ -35,6 +35,14 @@
 // Each workgroup writes its O normalised by its own denominator (bf16) with
 // its reference and denominator (fp32); a second kernel combines the splits
 // (the same algebra as one pass, in fp32).
+//
+// For the layer pipeline (copy of layer l+1 under the attention of layer l,
+// "vLLM Hybrid HiSparse 源码实现分析" section 6), a second instance of the
+// kernel takes extra workgroups after the decode's: first some that copy the
+// next layer's misses from pinned host memory, then some that combine the
+// previous layer's splits with the combine kernel's own function.  They run
+// on the CUs the decode leaves free and on those its workgroups release, in
+// the same launch, so the pipeline needs no second stream.
 #include "common.h"
 #include "kernels.h"
 
