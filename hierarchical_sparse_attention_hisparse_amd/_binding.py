@@ -165,7 +165,9 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False):
+def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False, device=None):
+    """Checks one device tensor and returns its address.  `device`: the
+    pool's device index (the library checks that it is the current one)."""
     import torch
     if t is None:
         if allow_none:
@@ -173,9 +175,9 @@ def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False):
         raise ValueError("%s is required" % name)
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a device (cuda) tensor" % name)
-    if t.device.index != torch.cuda.current_device():
-        raise ValueError("%s is on cuda:%d, not on the current device cuda:%d"
-                         % (name, t.device.index, torch.cuda.current_device()))
+    if device is not None and t.get_device() != device:
+        raise ValueError("%s is on cuda:%d, not on the pool's device cuda:%d"
+                         % (name, t.get_device(), device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
@@ -186,10 +188,11 @@ def _dev(t, dtype, shape: Optional[Sequence[int]], name: str, allow_none=False):
 
 
 class _Pool:
-    def __init__(self, handle: int, cfg: PoolConfig, device_pool_rows: int, keep=()):
+    def __init__(self, handle: int, cfg: PoolConfig, device_pool_rows: int, device: int, keep=()):
         self.handle = handle
         self.cfg = cfg
         self.device_pool_rows = device_pool_rows
+        self.device = device
         # The library keeps raw pointers to the device pools and host buffers:
         # hold them for as long as the pool lives.
         self._keep = tuple(keep)
@@ -211,8 +214,10 @@ def hisparse_init_pool(config: PoolConfig, host_pools, host_pool_rows, device_po
         hp[l] = addr
     rows = (ctypes.c_int64 * L)(*[int(x) for x in host_pool_rows])
     dp = (ctypes.c_void_p * L)()
+    cur = torch.cuda.current_device()
     for l, d in enumerate(device_pools):
-        dp[l] = _dev(d, torch.uint8, (device_pool_rows, config.row_bytes), "device_pools[%d]" % l)
+        dp[l] = _dev(d, torch.uint8, (device_pool_rows, config.row_bytes), "device_pools[%d]" % l,
+                     device=cur)
     c = config._c()
     out = ctypes.c_void_p()
     _check_rc(load_library().hisparse_init_pool(ctypes.byref(c), ctypes.cast(hp, ctypes.c_void_p),
@@ -220,7 +225,8 @@ def hisparse_init_pool(config: PoolConfig, host_pools, host_pool_rows, device_po
                                                  ctypes.cast(dp, ctypes.c_void_p),
                                                  device_pool_rows, ctypes.byref(out)),
               "hisparse_init_pool")
-    return _Pool(int(out.value), config, device_pool_rows, keep=list(device_pools) + list(host_pools))
+    return _Pool(int(out.value), config, device_pool_rows, cur,
+                 keep=list(device_pools) + list(host_pools))
 
 
 def hisparse_destroy_pool(pool: _Pool):
@@ -239,17 +245,17 @@ def _resolve_ptrs(pool, batch, top_k, req_idx, top_k_tokens, seq_lens, host_cach
     max_pages = (c.max_seq_len + c.page_size - 1) // c.page_size if c.page_size > 0 else 0
     lead = () if steps is None else (steps,)
     return [
-        _dev(req_idx, torch.int32, (batch,), "req_idx"),
-        _dev(top_k_tokens, torch.int32, lead + (batch, top_k), "top_k_tokens"),
-        _dev(seq_lens, torch.int32, lead + (batch,), "seq_lens"),
-        _dev(host_cache_locs, torch.int64, (R, c.max_seq_len), "host_cache_locs"),
+        _dev(req_idx, torch.int32, (batch,), "req_idx", device=pool.device),
+        _dev(top_k_tokens, torch.int32, lead + (batch, top_k), "top_k_tokens", device=pool.device),
+        _dev(seq_lens, torch.int32, lead + (batch,), "seq_lens", device=pool.device),
+        _dev(host_cache_locs, torch.int64, (R, c.max_seq_len), "host_cache_locs", device=pool.device),
         _dev(resident_block_table, torch.int32, (R, max_pages), "resident_block_table",
-             allow_none=True),
-        _dev(slot_tokens, torch.int32, (R, S), "slot_tokens"),
-        _dev(lru_slots, torch.int32, (R, S), "lru_slots"),
-        _dev(lru_clock, torch.int32, (R,), "lru_clock"),
-        _dev(device_buffer_locs, torch.int32, lead + (batch, top_k), "device_buffer_locs"),
-        _dev(stats, torch.int64, (5,), "stats", allow_none=True),
+             allow_none=True, device=pool.device),
+        _dev(slot_tokens, torch.int32, (R, S), "slot_tokens", device=pool.device),
+        _dev(lru_slots, torch.int32, (R, S), "lru_slots", device=pool.device),
+        _dev(lru_clock, torch.int32, (R,), "lru_clock", device=pool.device),
+        _dev(device_buffer_locs, torch.int32, lead + (batch, top_k), "device_buffer_locs", device=pool.device),
+        _dev(stats, torch.int64, (5,), "stats", allow_none=True, device=pool.device),
     ]
 
 
@@ -271,7 +277,7 @@ def hisparse_gather_copy_step(pool, stream, step, batch, layer_begin=0, layer_en
     import torch
     if layer_end is None:
         layer_end = pool.cfg.num_layers
-    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True, device=pool.device)
     _check_rc(load_library().hisparse_gather_copy_step(pool.handle, _stream_handle(stream), step,
                                                        batch, layer_begin, layer_end, sp),
               "hisparse_gather_copy_step")
@@ -303,7 +309,7 @@ def hisparse_gather_copy(pool, stream, batch, layer_begin=0, layer_end=None, sta
     import torch
     if layer_end is None:
         layer_end = pool.cfg.num_layers
-    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True, device=pool.device)
     _check_rc(load_library().hisparse_gather_copy(pool.handle, _stream_handle(stream), batch,
                                                   layer_begin, layer_end, sp),
               "hisparse_gather_copy")
@@ -317,9 +323,9 @@ def hisparse_mirror_rows(pool, stream, dev_rows, host_rows, layer_begin=0, layer
     if layer_end is None:
         layer_end = pool.cfg.num_layers
     n = int(dev_rows.shape[0])
-    dp = _dev(dev_rows, torch.int32, (n,), "dev_rows")
-    hp = _dev(host_rows, torch.int64, (n,), "host_rows")
-    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    dp = _dev(dev_rows, torch.int32, (n,), "dev_rows", device=pool.device)
+    hp = _dev(host_rows, torch.int64, (n,), "host_rows", device=pool.device)
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True, device=pool.device)
     _check_rc(load_library().hisparse_mirror_rows(pool.handle, _stream_handle(stream), n, dp, hp,
                                                   layer_begin, layer_end, sp),
               "hisparse_mirror_rows")
@@ -331,12 +337,12 @@ def hisparse_invalidate_tokens(pool, stream, req_rows, tok_begin, tok_end, slot_
     import torch
     n = int(req_rows.shape[0])
     R, S = pool.cfg.max_requests, pool.cfg.slots
-    rp = _dev(req_rows, torch.int32, (n,), "req_rows")
-    bp = _dev(tok_begin, torch.int32, (n,), "tok_begin")
-    ep = _dev(tok_end, torch.int32, (n,), "tok_end")
-    stp = _dev(slot_tokens, torch.int32, (R, S), "slot_tokens")
-    lp = _dev(lru_slots, torch.int32, (R, S), "lru_slots")
-    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    rp = _dev(req_rows, torch.int32, (n,), "req_rows", device=pool.device)
+    bp = _dev(tok_begin, torch.int32, (n,), "tok_begin", device=pool.device)
+    ep = _dev(tok_end, torch.int32, (n,), "tok_end", device=pool.device)
+    stp = _dev(slot_tokens, torch.int32, (R, S), "slot_tokens", device=pool.device)
+    lp = _dev(lru_slots, torch.int32, (R, S), "lru_slots", device=pool.device)
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True, device=pool.device)
     _check_rc(load_library().hisparse_invalidate_tokens(pool.handle, _stream_handle(stream), n, rp,
                                                         bp, ep, stp, lp, sp),
               "hisparse_invalidate_tokens")
@@ -348,10 +354,10 @@ def hisparse_invalidate_host_rows(pool, stream, rows_sorted, host_cache_locs, sl
     import torch
     n = int(rows_sorted.shape[0])
     R, S = pool.cfg.max_requests, pool.cfg.slots
-    rp = _dev(rows_sorted, torch.int64, (n,), "rows_sorted")
-    lp_ = _dev(host_cache_locs, torch.int64, (R, pool.cfg.max_seq_len), "host_cache_locs")
-    stp = _dev(slot_tokens, torch.int32, (R, S), "slot_tokens")
-    lp = _dev(lru_slots, torch.int32, (R, S), "lru_slots")
+    rp = _dev(rows_sorted, torch.int64, (n,), "rows_sorted", device=pool.device)
+    lp_ = _dev(host_cache_locs, torch.int64, (R, pool.cfg.max_seq_len), "host_cache_locs", device=pool.device)
+    stp = _dev(slot_tokens, torch.int32, (R, S), "slot_tokens", device=pool.device)
+    lp = _dev(lru_slots, torch.int32, (R, S), "lru_slots", device=pool.device)
     _check_rc(load_library().hisparse_invalidate_host_rows(pool.handle, _stream_handle(stream), n,
                                                            rp, lp_, stp, lp),
               "hisparse_invalidate_host_rows")
@@ -360,9 +366,9 @@ def hisparse_invalidate_host_rows(pool, stream, rows_sorted, host_cache_locs, sl
 def hisparse_sparse_mla_decode(pool, stream, batch, heads, top_k, layer, q_bf16,
                                device_buffer_locs, softmax_scale, out_bf16):
     import torch
-    qp = _dev(q_bf16, torch.bfloat16, (batch, heads, 576), "q_bf16")
-    lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs")
-    op = _dev(out_bf16, torch.bfloat16, (batch, heads, 512), "out_bf16")
+    qp = _dev(q_bf16, torch.bfloat16, (batch, heads, 576), "q_bf16", device=pool.device)
+    lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs", device=pool.device)
+    op = _dev(out_bf16, torch.bfloat16, (batch, heads, 512), "out_bf16", device=pool.device)
     _check_rc(load_library().hisparse_sparse_mla_decode(pool.handle, _stream_handle(stream),
                                                         batch, heads, top_k, layer, qp, lp,
                                                         ctypes.c_float(softmax_scale), op),
@@ -378,12 +384,12 @@ def hisparse_decode_layers_overlapped(pool, stream, batch, heads, top_k, q_per_l
     L = pool.cfg.num_layers
     if len(q_per_layer) != L or len(out_per_layer) != L:
         raise ValueError("need one query and one output tensor per layer")
-    qs = (ctypes.c_void_p * L)(*[_dev(q, torch.bfloat16, (batch, heads, 576), "q_bf16[%d]" % l)
+    qs = (ctypes.c_void_p * L)(*[_dev(q, torch.bfloat16, (batch, heads, 576), "q_bf16[%d]" % l, device=pool.device)
                                  for l, q in enumerate(q_per_layer)])
-    outs = (ctypes.c_void_p * L)(*[_dev(o, torch.bfloat16, (batch, heads, 512), "out_bf16[%d]" % l)
+    outs = (ctypes.c_void_p * L)(*[_dev(o, torch.bfloat16, (batch, heads, 512), "out_bf16[%d]" % l, device=pool.device)
                                    for l, o in enumerate(out_per_layer)])
-    lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs")
-    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True)
+    lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs", device=pool.device)
+    sp = _dev(stats, torch.int64, (5,), "stats", allow_none=True, device=pool.device)
     _check_rc(load_library().hisparse_decode_layers_overlapped(
         pool.handle, _stream_handle(stream), batch, heads, top_k, ctypes.cast(qs, ctypes.c_void_p), lp, ctypes.c_float(softmax_scale),
         ctypes.cast(outs, ctypes.c_void_p), sp), "hisparse_decode_layers_overlapped")
