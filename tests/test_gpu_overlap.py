@@ -78,3 +78,38 @@ def test_overlapped_layers_match_sequential(B, L, corrupt):
     finally:
         seq.close()
         ovl.close()
+
+
+def test_overlapped_rejects_bad_layer_before_enqueueing():
+    """Every layer's arguments are checked before anything is enqueued: a
+    misaligned query of the last layer is refused (EINVAL) and no layer's
+    device pool or the stats have changed (layer 0's copy never ran)."""
+    import ctypes
+    print("[overlap] bad last layer", flush=True)
+    L, H, B = 3, 32, 4
+    w = synth("ovl_bad", 91, R=B, S=256, k=128, steps=1, n0=[3000, 3500, 4000, 4500], L=L)
+    pair = Pair(w, make_host_pools(w, kind="mla"), with_oracle=False)
+    try:
+        pair.pre_step_writes(0)
+        hs.hisparse_resolve_plan(pair.pool, None, w.B, w.k, pair.req_idx, pair.topk[0], pair.seq[0],
+                                 pair.locs, pair.bt, pair.st, pair.lru, pair.clk, pair.out, pair.stats)
+        torch.cuda.synchronize()
+        before = [d.clone() for d in pair.dev_pools]
+        stats_before = pair.stats.clone()
+        qs = [make_queries(w.B, H, seed=l, device="cuda") for l in range(L)]
+        outs = [torch.empty((w.B, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        qp = (ctypes.c_void_p * L)(*[q.data_ptr() for q in qs])
+        qp[L - 1] = qs[L - 1].data_ptr() + 2          # not 16-byte aligned
+        op = (ctypes.c_void_p * L)(*[o.data_ptr() for o in outs])
+        lib = hs.load_library()
+        rc = lib.hisparse_decode_layers_overlapped(
+            ctypes.c_void_p(pair.pool.handle), None, w.B, H, w.k, ctypes.cast(qp, ctypes.c_void_p),
+            ctypes.c_void_p(pair.out.data_ptr()), ctypes.c_float(SCALE),
+            ctypes.cast(op, ctypes.c_void_p), ctypes.c_void_p(pair.stats.data_ptr()))
+        torch.cuda.synchronize()
+        assert rc == -1 and "aligned" in hs.hisparse_last_error()
+        for l in range(L):
+            assert torch.equal(before[l], pair.dev_pools[l]), "layer %d changed" % l
+        assert torch.equal(stats_before, pair.stats)
+    finally:
+        pair.close()
