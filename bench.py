@@ -95,7 +95,7 @@ def setup_gpu(w, torch, hs, host_buf):
     cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
                         row_bytes=w.row_bytes, num_layers=w.L, page_size=w.P,
                         resident_pages=w.resident_pages, max_seq_len=w.max_seq_len,
-                        max_steps=2)
+                        max_steps=2, max_heads=DECODE_HEADS)
     pool = hs.hisparse_init_pool(cfg, [host_buf], [w.host_pool_rows], pools, w.dev_pool_rows)
     st, lru, clk, dst, src = admission(w)
     # the forward pass's KV writes of fast-path requests for every step, ahead
@@ -358,7 +358,8 @@ def next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, warmup, ste
     pools4 = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)
               for _ in range(L)]
     cfg4 = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
-                         row_bytes=w.row_bytes, num_layers=L, max_seq_len=w.max_seq_len)
+                         row_bytes=w.row_bytes, num_layers=L, max_seq_len=w.max_seq_len,
+                         max_heads=DECODE_HEADS)
     pool4 = hs.hisparse_init_pool(cfg4, [host_buf] + extra, [w.host_pool_rows] * L, pools4,
                                   w.dev_pool_rows)
     qs = [make_queries(w.B, DECODE_HEADS, seed=80 + l, device="cuda") for l in range(L)]

@@ -28,6 +28,7 @@ class _Config(ctypes.Structure):
         ("max_top_k", ctypes.c_int32), ("max_batch", ctypes.c_int32),
         ("row_bytes", ctypes.c_int32), ("num_layers", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("max_steps", ctypes.c_int32),
+        ("max_heads", ctypes.c_int32),
         ("resident_pages", ctypes.c_int64), ("max_seq_len", ctypes.c_int64),
     ]
 
@@ -44,11 +45,12 @@ class PoolConfig:
     resident_pages: int = 0
     max_seq_len: int = 0
     max_steps: int = 1
+    max_heads: int = 0   # largest decode `heads` (multiple of 16); 0 = no decode workspace
 
     def _c(self) -> _Config:
         return _Config(self.max_requests, self.slots, self.max_top_k, self.max_batch,
                        self.row_bytes, self.num_layers, self.page_size, self.max_steps,
-                       self.resident_pages, self.max_seq_len)
+                       self.max_heads, self.resident_pages, self.max_seq_len)
 
 
 def library_path() -> str:
@@ -378,8 +380,10 @@ def hisparse_sparse_mla_decode(pool, stream, batch, heads, top_k, layer, q_bf16,
 def hisparse_decode_layers_overlapped(pool, stream, batch, heads, top_k, q_per_layer,
                                       device_buffer_locs, softmax_scale, out_per_layer,
                                       stats=None):
-    """Per-layer miss copy pipelined with per-layer decode on the pool's two
-    streams, after a plan on ``stream``; ``stream`` waits for both."""
+    """Per-layer miss copy pipelined with per-layer decode, after a plan on
+    ``stream``: layer 0's copy, then one launch per layer that decodes layer
+    l while spare workgroups copy layer l + 1 and combine layer l - 1, all
+    enqueued on ``stream`` alone."""
     import torch
     L = pool.cfg.num_layers
     if len(q_per_layer) != L or len(out_per_layer) != L:

@@ -3,6 +3,7 @@
 // kernel launches.  No entry point that takes a stream synchronises or reads
 // device memory back.
 #include <hip/hip_runtime.h>
+#include <inttypes.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -27,8 +28,9 @@ struct hisparse_pool {
   unsigned char** d_dev_ptrs;   // [L]
   int64_t* d_host_rows;         // [L]
   uint4* zero_row;              // row_bytes of zeros (source of out-of-range host rows)
-  void* dec_ws;                 // decode split partials, grown on demand
+  void* dec_ws;                 // decode split partials (two halves), sized at init
   size_t dec_ws_bytes;
+  int32_t* plan_batch;          // host: batch of the last plan of each slice (-1: none)
   // host copies
   unsigned char** dev_ptrs;     // [L]
   unsigned char** host_ptrs;    // [L] device-mapped host pool pointers
@@ -138,7 +140,36 @@ int launch_plan(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   p.copy_layers = copy_layers;
   hipError_t e = launch_resolve(p, batch, stream);
   if (e != hipSuccess) return hip_fail(e, "resolve kernel launch");
+  pool->plan_batch[slice] = batch;
   return HISPARSE_OK;
+}
+
+// A copy replays plan slice `slice`: its batch must be the plan's, or rows
+// of an older, larger plan would be copied over slots that now hold others.
+int check_plan_batch(const hisparse_pool* pool, int32_t batch, int32_t slice) {
+  const int32_t pb = pool->plan_batch[slice];
+  if (pb < 0) return fail(HISPARSE_EINVAL, "no plan has been enqueued into plan slice %d", slice);
+  if (batch != pb)
+    return fail(HISPARSE_EINVAL, "batch %d differs from the batch %d of the plan in slice %d", batch,
+                pb, slice);
+  return HISPARSE_OK;
+}
+
+// MemAvailable of /proc/meminfo in bytes, or -1 if it cannot be read.
+int64_t host_mem_available() {
+  FILE* f = fopen("/proc/meminfo", "r");
+  if (!f) return -1;
+  char line[256];
+  int64_t kb = -1;
+  while (fgets(line, sizeof line, f)) {
+    long long v = 0;
+    if (sscanf(line, "MemAvailable: %lld kB", &v) == 1) {
+      kb = (int64_t)v;
+      break;
+    }
+  }
+  fclose(f);
+  return kb < 0 ? -1 : kb * 1024;
 }
 
 // Workgroups per batch row of the copy: about 4096 wavefronts in total.
@@ -177,6 +208,12 @@ int hisparse_host_alloc(size_t bytes, void** out) {
   if (!out) return fail(HISPARSE_EINVAL, "out is NULL");
   *out = nullptr;
   if (bytes == 0) return fail(HISPARSE_EINVAL, "bytes is 0");
+  const int64_t avail = host_mem_available();
+  if (avail >= 0 && (double)bytes > 0.95 * (double)avail)
+    return fail(HISPARSE_ENOMEM,
+                "%zu bytes of pinned host memory exceed 95%% of the host's MemAvailable "
+                "(%" PRId64 " bytes)",
+                bytes, avail);
   void* p = nullptr;
   hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
   if (e != hipSuccess || p == nullptr)
@@ -211,6 +248,8 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   if (c.num_layers <= 0) return fail(HISPARSE_EINVAL, "num_layers must be > 0");
   if (c.page_size < 0 || c.resident_pages < 0 || c.max_steps < 0)
     return fail(HISPARSE_EINVAL, "page_size / resident_pages / max_steps must be >= 0");
+  if (c.max_heads < 0 || c.max_heads % 16 != 0 || c.max_heads > 65536)
+    return fail(HISPARSE_EINVAL, "max_heads %d must be a multiple of 16 in [0, 65536]", c.max_heads);
   if (c.resident_pages > 0 && c.page_size == 0)
     return fail(HISPARSE_EINVAL, "resident_pages > 0 needs page_size > 0");
   if (c.max_seq_len <= 0 || c.max_seq_len > INT32_MAX)
@@ -289,6 +328,15 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   memcpy(pool->host_rows, host_pool_rows, (size_t)L * sizeof(int64_t));
 
   const size_t slices = c.max_steps > 1 ? (size_t)c.max_steps : 1;  // one plan per verification step
+  pool->plan_batch = (int32_t*)malloc(slices * sizeof(int32_t));
+  if (!pool->plan_batch) {
+    free(pool->host_rows);
+    free(hdev);
+    free(ddev);
+    free(pool);
+    return fail(HISPARSE_ENOMEM, "host allocation failed");
+  }
+  for (size_t q = 0; q < slices; ++q) pool->plan_batch[q] = -1;
   const size_t entries = (size_t)c.max_batch * c.max_top_k * slices;
   const size_t bytes_src = entries * 8, bytes_dst = entries * 4;
   const size_t bytes_cnt = (size_t)c.max_batch * slices * 4;
@@ -298,6 +346,7 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
                        3 * align16(bytes_tab) + align16((size_t)c.row_bytes);
   e = hipMalloc((void**)&ws, total);
   if (e != hipSuccess) {
+    free(pool->plan_batch);
     free(pool->host_rows);
     free(hdev);
     free(ddev);
@@ -322,11 +371,30 @@ int hisparse_init_pool(const hisparse_pool_config* cfg, void* const* host_pools,
   if (e == hipSuccess) e = prepare_maintain();
   if (e != hipSuccess) {
     (void)hipFree(ws);
+    free(pool->plan_batch);
     free(pool->host_rows);
     free(hdev);
     free(ddev);
     free(pool);
     return hip_fail(e, "pool set-up");
+  }
+  // The decode's split workspace, two halves (the layer pipeline alternates
+  // them), sized for every shape the configuration admits.
+  if (c.max_heads > 0) {
+    const size_t dbytes = 2 * decode_workspace_max_bytes(c.max_batch, c.max_heads);
+    e = hipMalloc(&pool->dec_ws, dbytes);
+    if (e != hipSuccess || !pool->dec_ws) {
+      (void)hipGetLastError();
+      (void)hipFree(ws);
+      free(pool->plan_batch);
+      free(pool->host_rows);
+      free(hdev);
+      free(ddev);
+      free(pool);
+      return fail(HISPARSE_ENOMEM, "hipMalloc(%zu) for the decode workspace: %s", dbytes,
+                  hipGetErrorString(e));
+    }
+    pool->dec_ws_bytes = dbytes;
   }
   *out = pool;
   return ok();
@@ -339,6 +407,7 @@ void hisparse_destroy_pool(hisparse_pool* pool) {
   free(pool->dev_ptrs);
   free(pool->host_ptrs);
   free(pool->host_rows);
+  free(pool->plan_batch);
   free(pool);
 }
 
@@ -370,8 +439,9 @@ int hisparse_gather_copy(hisparse_pool* pool, void* stream, int32_t batch, int32
                 pool->cfg.num_layers);
   if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
   if (batch == 0 || layer_begin == layer_end) return ok();
-  int rc = check_device(pool);
+  int rc = check_plan_batch(pool, batch, 0);
   if (rc != HISPARSE_OK) return rc;
+  if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
   rc = launch_copy(pool, (hipStream_t)stream, batch, layer_begin, layer_end, stats);
   return rc == HISPARSE_OK ? ok() : rc;
 }
@@ -454,8 +524,9 @@ int hisparse_gather_copy_step(hisparse_pool* pool, void* stream, int32_t step, i
                 pool->cfg.num_layers);
   if (stats && !aligned(stats, 8)) return fail(HISPARSE_EINVAL, "stats is not 8-byte aligned");
   if (batch == 0 || layer_begin == layer_end) return ok();
-  int rc = check_device(pool);
+  int rc = check_plan_batch(pool, batch, step);
   if (rc != HISPARSE_OK) return rc;
+  if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
   rc = launch_copy(pool, (hipStream_t)stream, batch, layer_begin, layer_end, stats, step);
   return rc == HISPARSE_OK ? ok() : rc;
 }
@@ -554,9 +625,13 @@ static int decode_check(hisparse_pool* pool, int32_t batch, int32_t heads, int32
                         int32_t layer, const void* q_bf16, const int32_t* device_buffer_locs,
                         void* out_bf16) {
   if (!pool) return fail(HISPARSE_EINVAL, "pool is NULL");
-  if (batch < 0) return fail(HISPARSE_EINVAL, "batch %d < 0", batch);
+  if (batch < 0 || batch > pool->cfg.max_batch)
+    return fail(HISPARSE_EINVAL, "batch %d outside [0, max_batch=%d]", batch, pool->cfg.max_batch);
   if (heads <= 0 || heads % 16 != 0)
     return fail(HISPARSE_EUNSUPPORTED, "heads %d must be a positive multiple of 16", heads);
+  if (heads > pool->cfg.max_heads)
+    return fail(HISPARSE_EINVAL, "heads %d exceed the pool's max_heads %d (its decode workspace)",
+                heads, pool->cfg.max_heads);
   if (top_k < 0 || top_k > pool->cfg.max_top_k)
     return fail(HISPARSE_EINVAL, "top_k %d outside [0, max_top_k=%d]", top_k, pool->cfg.max_top_k);
   if (layer < 0 || layer >= pool->cfg.num_layers)
@@ -586,35 +661,23 @@ static int decode_launch(hisparse_pool* pool, hipStream_t stream, int32_t batch,
                          void* comb_out = nullptr, bool defer = false) {
   const int splits = decode_splits(batch, heads, top_k);
   const size_t one = decode_workspace_bytes(batch, heads, splits);
-  const size_t need = half >= 0 ? 2 * one : one;
-  if (need > pool->dec_ws_bytes) {  // grow the split workspace (synchronises the device)
-    if (pool->dec_ws) {
-      hipError_t fe = hipFree(pool->dec_ws);
-      pool->dec_ws = nullptr;
-      pool->dec_ws_bytes = 0;
-      if (fe != hipSuccess) return hip_fail(fe, "hipFree of the decode workspace");
-    }
-    void* w = nullptr;
-    hipError_t me = hipMalloc(&w, need);
-    if (me != hipSuccess || !w) {
-      (void)hipGetLastError();
-      return fail(HISPARSE_ENOMEM, "hipMalloc(%zu) for the decode workspace: %s", need,
-                  hipGetErrorString(me));
-    }
-    pool->dec_ws = w;
-    pool->dec_ws_bytes = need;
-  }
+  // Each half holds the largest shape the configuration admits (checked by
+  // decode_check), so this is an internal invariant, not a caller error.
+  const size_t half_bytes = pool->dec_ws_bytes / 2;
+  if (one > half_bytes)
+    return fail(HISPARSE_EUNSUPPORTED, "decode workspace of %zu bytes exceeds the pool's %zu", one,
+                half_bytes);
   // each half: bf16 partial O, then fp32 (reference, denominator) per
   // (row, group, split, head)
   const size_t entries = one / (512 * sizeof(uint16_t) + 2 * sizeof(float));
   unsigned char* ws = (unsigned char*)pool->dec_ws;
-  unsigned char* mine = ws + (half > 0 ? one : 0);
+  unsigned char* mine = ws + (half > 0 ? half_bytes : 0);
   DecodeParams d = {};
   d.splits = splits;
   d.part_o = (uint16_t*)mine;
   d.part_ml = (float*)(d.part_o + entries * 512);
   if (comb_out) {
-    unsigned char* other = ws + (half > 0 ? 0 : one);
+    unsigned char* other = ws + (half > 0 ? 0 : half_bytes);
     d.comb_part_o = (const uint16_t*)other;
     d.comb_part_ml = (const float*)(d.comb_part_o + entries * 512);
     d.comb_out = (uint16_t*)comb_out;
@@ -675,6 +738,7 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t
     if ((rc = decode_check(pool, batch, heads, top_k, l, q_bf16[l], device_buffer_locs,
                            out_bf16[l])) != HISPARSE_OK)
       return rc;
+  if ((rc = check_plan_batch(pool, batch, 0)) != HISPARSE_OK) return rc;
   if ((rc = check_device(pool)) != HISPARSE_OK) return rc;
   // All on the caller's stream, so no cross-stream events: layer 0's copy
   // alone, then one launch per layer that decodes layer l while its spare

@@ -10,14 +10,8 @@ namespace hisparse {
 constexpr int kWave = 64;
 
 // Launch shapes and LDS limits of the resolver.
-#ifndef HISPARSE_RESOLVE_THREADS
-#define HISPARSE_RESOLVE_THREADS 1024
-#endif
-#ifndef HISPARSE_HASH_FACTOR
-#define HISPARSE_HASH_FACTOR 4
-#endif
-constexpr int kResolveThreads = HISPARSE_RESOLVE_THREADS;  // threads per request row
-constexpr int kHashFactor = HISPARSE_HASH_FACTOR;          // table cells per top-k entry
+constexpr int kResolveThreads = 1024;  // threads per request row
+constexpr int kHashFactor = 4;         // table cells per top-k entry
 constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxSlots = 16384;
@@ -29,23 +23,14 @@ constexpr int kVictimRounds = 4;                      // min-extraction rounds b
 constexpr int kCopyThreads = 256;
 
 // Smallest batch whose miss copy runs inside the plan kernel.
-#ifndef HISPARSE_FUSE_MIN_BATCH
-#define HISPARSE_FUSE_MIN_BATCH 8
-#endif
-constexpr int kFuseMinBatch = HISPARSE_FUSE_MIN_BATCH;
+constexpr int kFuseMinBatch = 8;
 constexpr int kMaxFusedLayers = 8;    // layers whose pointers fit the kernel arguments
 constexpr int kCopyRowsInFlight = 3;  // rows per wavefront per iteration of the fused copy (measured: 1, 2, 4 and 8 slower)
 // The next layer's copy inside a decode launch (pipelined layer loop): rows
 // per wavefront per iteration, and about how many workgroups it adds to the
 // decode's (batch rows x chunks of each row's misses).
-#ifndef HISPARSE_LAYER_COPY_RIF
-#define HISPARSE_LAYER_COPY_RIF 8
-#endif
-constexpr int kLayerCopyRowsInFlight = HISPARSE_LAYER_COPY_RIF;
-#ifndef HISPARSE_LAYER_COPY_GROUPS
-#define HISPARSE_LAYER_COPY_GROUPS 128
-#endif
-constexpr int kLayerCopyGroups = HISPARSE_LAYER_COPY_GROUPS;
+constexpr int kLayerCopyRowsInFlight = 8;
+constexpr int kLayerCopyGroups = 128;
 constexpr int kLayerCombineGroups = 128;  // workgroups of the previous layer's combine in the same launch
 
 // Invalidation by host rows: sets up to this many rows are searched in LDS.

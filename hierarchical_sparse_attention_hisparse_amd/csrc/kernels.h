@@ -130,5 +130,6 @@ hipError_t launch_invalidate_host_rows(const InvalidateParams& p, hipStream_t st
 hipError_t prepare_maintain();
 int decode_splits(int batch, int heads, int k);
 size_t decode_workspace_bytes(int batch, int heads, int splits);
+size_t decode_workspace_max_bytes(int max_batch, int max_heads);
 
 }  // namespace hisparse

@@ -70,14 +70,8 @@ __global__ __launch_bounds__(256) void invalidate_tokens_kernel(InvalidateParams
 // lower bound of a fixed step count; a thread's searches advance together.
 // Measured on 72 requests x 4096 slots against 4096 rows: 512 x 1 takes
 // 9.6 us, 256 x 1 11.5, 1024 x 1 9.8, 512 x 2 11.8, 1024 x 4 15.3.
-#ifndef HISPARSE_INV_THREADS
-#define HISPARSE_INV_THREADS 512
-#endif
-#ifndef HISPARSE_INV_SLOTS
-#define HISPARSE_INV_SLOTS 1
-#endif
-constexpr int kInvThreads = HISPARSE_INV_THREADS;
-constexpr int kInvSlotsPerThread = HISPARSE_INV_SLOTS;
+constexpr int kInvThreads = 512;
+constexpr int kInvSlotsPerThread = 1;
 
 __device__ inline int lower_bound_fixed(const int64_t* rows, int count, int64_t h) {
   int base = 0, n = count;

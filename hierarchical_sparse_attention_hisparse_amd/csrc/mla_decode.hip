@@ -257,6 +257,11 @@ __device__ inline void combine_rows(const uint16_t* part_o, const float* part_ml
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
+  // A NaN score (a NaN code or scale in an attended row) leaves its split's
+  // denominator NaN; the softmax it belongs to is NaN, so is the output.
+  bool nan_l = false;
+#pragma unroll
+  for (int j = 0; j < NSMAX; ++j) nan_l |= j < NS && ml[j].y != ml[j].y;
   if (M != -INFINITY) {
 #pragma unroll
     for (int j = 0; j < NSMAX; ++j) {
@@ -272,7 +277,7 @@ __device__ inline void combine_rows(const uint16_t* part_o, const float* part_ml
       }
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = nan_l ? __builtin_nanf("") : L > 0.f ? 1.f / L : 0.f;
   uint4 w;
   w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
@@ -630,6 +635,15 @@ size_t decode_workspace_bytes(int batch, int heads, int splits) {
   const int HG = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
   const size_t entries = (size_t)batch * HG * splits * kHeadsPerGroup;
   return entries * (kLat * sizeof(uint16_t) + 2 * sizeof(float));
+}
+
+// The largest decode_workspace_bytes of any batch <= max_batch and heads <=
+// max_heads: decode_splits keeps batch * groups * splits <= 256 while
+// batch * groups <= 256, and takes one split beyond.
+size_t decode_workspace_max_bytes(int max_batch, int max_heads) {
+  const int HG = (max_heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const size_t units = (size_t)max_batch * HG > 256 ? (size_t)max_batch * HG : 256;
+  return units * kHeadsPerGroup * (kLat * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t prepare_sparse_mla_decode() {

@@ -87,6 +87,12 @@ typedef struct {
   int32_t max_steps;      /* verification steps per hisparse_resolve_steps call
                              (speculative decoding); 0 or 1 = one.  The miss
                              plan workspace holds this many slices.             */
+  int32_t max_heads;      /* largest `heads` of any decode call (a multiple of
+                             16), or 0 if the pool never decodes.  Sizes the
+                             decode's split workspace, allocated at init:
+                             2 * max(256, max_batch * ceil(max_heads/128))
+                             * 132096 bytes (67.6 MB at max_batch <= 256 and
+                             max_heads <= 128).                                 */
   int64_t resident_pages; /* resident pages in each device pool (0 if P == 0)   */
   int64_t max_seq_len;    /* row stride, in tokens, of host_cache_locs and
                              (divided by P, rounded up) of the block table      */
@@ -99,8 +105,12 @@ typedef struct {
  *   page, ownership table).  The memory is page-locked, mapped into the
  *   device address space, and 4096-byte aligned.  Host pools given to
  *   hisparse_init_pool must come from here (or from another hipHostMalloc).
- *   Returns ENOMEM if the allocation fails.  hisparse_host_free(NULL) is a
- *   no-op.
+ *   A request above 95% of the host's available memory (MemAvailable in
+ *   /proc/meminfo) is refused with ENOMEM before anything is pinned, as the
+ *   worker of "vLLM Hybrid HiSparse 源码实现分析" (section 2.4) refuses to
+ *   start when the host pool would not fit in RAM; pinning nearly all of RAM
+ *   would leave the host to the out-of-memory killer.  Returns ENOMEM if the
+ *   allocation fails.  hisparse_host_free(NULL) is a no-op.
  */
 int hisparse_host_alloc(size_t bytes, void** out);
 int hisparse_host_free(void* ptr);
@@ -120,9 +130,12 @@ int hisparse_host_free(void* ptr);
  *   device_pool_rows   >= R*S + resident_pages*P and < 2^31.
  *   out                receives the pool.  The pool allocates its miss-plan
  *                      workspace in device memory (12 bytes per
- *                      max_batch*max_top_k entry) and frees it on destroy.
- *   Errors: EINVAL (shape, alignment, a host pool that is not pinned),
- *   ENOMEM, EHIP.  Must be called with the target device current.
+ *                      max_batch*max_top_k entry per plan slice) and, when
+ *                      max_heads > 0, the decode's split workspace; it frees
+ *                      both on destroy.  No later call allocates.
+ *   Errors: EINVAL (shape, alignment, a host pool that is not pinned,
+ *   max_heads not a multiple of 16), ENOMEM, EHIP.  Must be called with the
+ *   target device current.
  */
 int hisparse_init_pool(const hisparse_pool_config* config,
                        void* const* host_pools, const int64_t* host_pool_rows,
@@ -205,8 +218,11 @@ int hisparse_resolve_plan(hisparse_pool* pool, void* stream, int32_t batch,
  * pools of layers [layer_begin, layer_end).  Layers that share one index
  * replay the same plan and copy only their own bytes ("vLLM Hybrid HiSparse
  * 源码实现分析" section 7.4, follower layers).  `batch` must equal the batch
- * of the plan.  stats may be NULL (tripwires are then not counted).
- * Errors: EINVAL for a layer range outside [0, L) or batch > max_batch.
+ * of the last plan enqueued on this pool (checked on the host: a different
+ * batch would replay rows of an older plan).  stats may be NULL (tripwires
+ * are then not counted).
+ * Errors: EINVAL for a layer range outside [0, L), a batch other than the
+ * plan's, or no plan yet.
  */
 int hisparse_gather_copy(hisparse_pool* pool, void* stream, int32_t batch,
                          int32_t layer_begin, int32_t layer_end,
@@ -225,15 +241,15 @@ int hisparse_gather_copy(hisparse_pool* pool, void* stream, int32_t batch,
  *   0 <= loc < device_pool_rows (O = 0 if there are none).
  *   q_bf16   device bf16 [batch][heads][576]
  *   out_bf16 device bf16 [batch][heads][512]
- * Requires row_bytes >= 656, heads a multiple of 16, top_k <= max_top_k.
- * The keys of each row are split across workgroups and a second kernel
- * combines the partial results; their workspace (about 129 KB per batch
- * row, 128-head group and split, with up to 256 / (batch * groups) splits)
- * is allocated by the pool on the first call that needs more than it holds:
- * that call synchronises the device, later calls of the same or a smaller
- * shape allocate nothing.  Calls on one pool that overlap in time (different
- * streams) race on this workspace.  Errors: EINVAL, EUNSUPPORTED, ENOMEM,
- * EHIP.
+ * Requires row_bytes >= 656, heads a multiple of 16 and <= max_heads,
+ * batch <= max_batch, top_k <= max_top_k.  The keys of each row are split
+ * across workgroups and a second kernel combines the partial results, in
+ * the pool's split workspace sized at init (see max_heads): the call
+ * allocates nothing and never synchronises.  Calls on one pool that overlap
+ * in time (different streams) race on this workspace.  A NaN in a row that
+ * is attended to (a 0x7F/0xFF latent code, a NaN scale) makes that row's
+ * outputs NaN, as the softmax of a NaN score is.  Errors: EINVAL,
+ * EUNSUPPORTED, EHIP.
  */
 int hisparse_sparse_mla_decode(hisparse_pool* pool, void* stream,
                                int32_t batch, int32_t heads, int32_t top_k,
@@ -337,8 +353,10 @@ int hisparse_invalidate_host_rows(hisparse_pool* pool, void* stream, int32_t cou
  * streams or events).  Results are those of hisparse_gather_copy of all
  * layers followed by hisparse_sparse_mla_decode of each layer l with
  * q_bf16[l] and out_bf16[l] (host arrays of L device pointers); stats[4]
- * counts the copy's tripwires.  Every layer's arguments are checked before
- * anything is enqueued.  Errors: as those calls.
+ * counts the copy's tripwires.  The split partials of consecutive layers
+ * use the two halves of the workspace sized at init, so nothing is
+ * allocated.  Every layer's arguments, and that batch equals the plan's,
+ * are checked before anything is enqueued.  Errors: as those calls.
  */
 int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t batch,
                                       int32_t heads, int32_t top_k, const void* const* q_bf16,

@@ -323,7 +323,9 @@ static double row_scale(const uint8_t* row, int blk) {
  *
  * Everything is computed in float64.  q is bf16 [batch][heads][576];
  * out is float64 [batch][heads][512].  A location >= dev_pool_rows is
- * skipped like -1.
+ * skipped like -1.  Each referenced row's K (and so V) is decoded to
+ * float64 once per batch row, and each query once per head, before the
+ * sums; the products and sums are the ones written above, in the same order.
  */
 int oracle_sparse_mla_decode(int32_t batch, int32_t heads, int32_t top_k,
                              const uint16_t* q, const int32_t* locs,
@@ -331,30 +333,45 @@ int oracle_sparse_mla_decode(int32_t batch, int32_t heads, int32_t top_k,
                              int32_t row_bytes, float softmax_scale,
                              double* out) {
   if (row_bytes < 656) return OR_EINVAL;
-  double* z = (double*)malloc(sizeof(double) * (size_t)(top_k > 0 ? top_k : 1));
-  if (!z) return OR_ENOMEM;
+  const size_t nk = (size_t)(top_k > 0 ? top_k : 1);
+  double* z = (double*)malloc(sizeof(double) * nk);
+  double* kd = (double*)malloc(sizeof(double) * nk * 576); /* K_i; V_i = its first 512 */
+  if (!z || !kd) {
+    free(z);
+    free(kd);
+    return OR_ENOMEM;
+  }
   const double scale = (double)softmax_scale;
+  double qd[576];
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t* lb = locs + (int64_t)b * top_k;
+    for (int32_t i = 0; i < top_k; ++i) {
+      int32_t loc = lb[i];
+      if (loc < 0 || (int64_t)loc >= dev_pool_rows) continue;
+      const uint8_t* row = dev_pool + (int64_t)loc * row_bytes;
+      double* ki = kd + (size_t)i * 576;
+      for (int d = 0; d < 512; ++d)
+        ki[d] = oracle_e4m3_to_double(row[d]) * row_scale(row, d / 128);
+      for (int d = 0; d < 64; ++d) {
+        uint16_t rv;
+        memcpy(&rv, row + 528 + 2 * d, sizeof rv);
+        ki[512 + d] = oracle_bf16_to_double(rv);
+      }
+    }
     for (int32_t h = 0; h < heads; ++h) {
       const uint16_t* qh = q + ((int64_t)b * heads + h) * 576;
       double* oh = out + ((int64_t)b * heads + h) * 512;
+      for (int d = 0; d < 576; ++d) qd[d] = oracle_bf16_to_double(qh[d]);
       for (int d = 0; d < 512; ++d) oh[d] = 0.0;
       double zmax = -INFINITY;
       int any = 0;
       for (int32_t i = 0; i < top_k; ++i) {
         int32_t loc = lb[i];
         if (loc < 0 || (int64_t)loc >= dev_pool_rows) continue;
-        const uint8_t* row = dev_pool + (int64_t)loc * row_bytes;
+        const double* ki = kd + (size_t)i * 576;
         double acc = 0.0;
-        for (int d = 0; d < 512; ++d)
-          acc += oracle_bf16_to_double(qh[d]) *
-                 (oracle_e4m3_to_double(row[d]) * row_scale(row, d / 128));
-        for (int d = 0; d < 64; ++d) {
-          uint16_t rv;
-          memcpy(&rv, row + 528 + 2 * d, sizeof rv);
-          acc += oracle_bf16_to_double(qh[512 + d]) * oracle_bf16_to_double(rv);
-        }
+        for (int d = 0; d < 512; ++d) acc += qd[d] * ki[d];         /* latent part */
+        for (int d = 0; d < 64; ++d) acc += qd[512 + d] * ki[512 + d]; /* rope part */
         z[i] = scale * acc;
         if (!any || z[i] > zmax) zmax = z[i];
         any = 1;
@@ -369,14 +386,14 @@ int oracle_sparse_mla_decode(int32_t batch, int32_t heads, int32_t top_k,
       for (int32_t i = 0; i < top_k; ++i) {
         int32_t loc = lb[i];
         if (loc < 0 || (int64_t)loc >= dev_pool_rows) continue;
-        const uint8_t* row = dev_pool + (int64_t)loc * row_bytes;
+        const double* vi = kd + (size_t)i * 576;
         double p = exp(z[i] - zmax) / denom;
-        for (int d = 0; d < 512; ++d)
-          oh[d] += p * (oracle_e4m3_to_double(row[d]) * row_scale(row, d / 128));
+        for (int d = 0; d < 512; ++d) oh[d] += p * vi[d];
       }
     }
   }
   free(z);
+  free(kd);
   return OR_OK;
 }
 

@@ -15,7 +15,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hisparse_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# HISPARSE_ORACLE_LIB names another build of the same source (the tests'
+# sanitizer run loads an ASan/UBSan build this way).
+_LIB = os.environ.get("HISPARSE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
@@ -137,9 +139,14 @@ def _host_addr(h):
 
 
 def oracle_sparse_mla_decode(q_bf16_bits, locs, dev_pool, softmax_scale: float,
-                             row_bytes: int = 656) -> np.ndarray:
+                             row_bytes: int = 656, threads: int = 0) -> np.ndarray:
     """Float64 attention output [B, H, 512] for bf16 queries given as uint16
-    bit patterns [B, H, 576] over the rows of ``dev_pool`` named by ``locs``."""
+    bit patterns [B, H, 576] over the rows of ``dev_pool`` named by ``locs``.
+
+    ``threads`` > 1 runs batch rows concurrently, each through the same C
+    function on its own rows (ctypes releases the GIL during the call); the
+    rows are independent, so the result is the same as one call over all
+    of them.  0 picks min(batch, CPU count, 16)."""
     lib = load_oracle()
     q = np.ascontiguousarray(q_bf16_bits, dtype=np.uint16)
     locs = np.ascontiguousarray(locs, dtype=np.int32)
@@ -148,13 +155,24 @@ def oracle_sparse_mla_decode(q_bf16_bits, locs, dev_pool, softmax_scale: float,
     k = locs.shape[1]
     out = np.empty((B, H, 512), dtype=np.float64)
     pool_addr = _host_addr(dev_pool)
-    rows = (dev_pool.shape[0] if isinstance(dev_pool, np.ndarray)
-            else dev_pool.shape[0])
-    rc = lib.oracle_sparse_mla_decode(B, H, k, _ptr(q), _ptr(locs), pool_addr,
-                                      rows, row_bytes, ctypes.c_float(softmax_scale),
-                                      _ptr(out))
-    if rc != 0:
-        raise ValueError("oracle_sparse_mla_decode failed (code %d)" % rc)
+    rows = dev_pool.shape[0]
+
+    def run(b0, b1):
+        rc = lib.oracle_sparse_mla_decode(b1 - b0, H, k, _ptr(q[b0:b1]), _ptr(locs[b0:b1]),
+                                          pool_addr, rows, row_bytes,
+                                          ctypes.c_float(softmax_scale), _ptr(out[b0:b1]))
+        if rc != 0:
+            raise ValueError("oracle_sparse_mla_decode failed (code %d)" % rc)
+
+    if threads == 0:
+        threads = min(B, os.cpu_count() or 1, 16)
+    if threads <= 1 or B <= 1:
+        run(0, B)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for f in [ex.submit(run, b, b + 1) for b in range(B)]:
+            f.result()
     return out
 
 

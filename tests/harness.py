@@ -32,10 +32,11 @@ class Pair:
     """The GPU side and the oracle side of one workload."""
 
     def __init__(self, w, host_bufs, with_oracle=True, max_batch=None, mode="resolve",
-                 max_steps=1):
+                 max_steps=1, max_heads=0):
         """mode "resolve": the single-call entry point (which copies inside the
         plan kernel at batch >= 8 with <= 8 layers); "split": the plan entry
-        point followed by the separate copy entry point."""
+        point followed by the separate copy entry point.  max_heads > 0 gives
+        the pool a decode workspace for up to that many heads."""
         assert mode in ("resolve", "split")
         self.mode = mode
         self.w = w
@@ -48,7 +49,8 @@ class Pair:
         cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k,
                             max_batch=max_batch or w.B, row_bytes=w.row_bytes,
                             num_layers=w.L, page_size=w.P, resident_pages=w.resident_pages,
-                            max_seq_len=w.max_seq_len, max_steps=max_steps)
+                            max_seq_len=w.max_seq_len, max_steps=max_steps,
+                            max_heads=max_heads)
         self.pool = hs.hisparse_init_pool(cfg, host_bufs, [w.host_pool_rows] * w.L,
                                           self.dev_pools, w.dev_pool_rows)
         st, lru, clk, dst, src = admission(w)

@@ -77,18 +77,14 @@ def test_decode_replayed_from_a_graph():
     locs_np = rng.integers(-1, rows, size=(B, k)).astype(np.int32)
     locs = torch.from_numpy(locs_np).cuda()
     hb = hs.HostBuffer(656 * 16)
-    cfg = hs.PoolConfig(max_requests=1, slots=k, max_top_k=k, max_batch=B, max_seq_len=16)
+    cfg = hs.PoolConfig(max_requests=1, slots=k, max_top_k=k, max_batch=B, max_seq_len=16,
+                        max_heads=H)
     pool = hs.hisparse_init_pool(cfg, [hb], [16], [dev], rows)
     scale = 1.0 / math.sqrt(192.0)
     try:
         qs = [make_queries(B, H, seed=30 + t, device="cuda") for t in range(3)]
-        want = []
-        for q in qs:  # eager calls (the first one also sizes the split workspace)
-            o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
-            hs.hisparse_sparse_mla_decode(pool, None, B, H, k, 0, q, locs, scale, o)
-            want.append(o)
-        torch.cuda.synchronize()
-
+        # The pool's first decode call is the captured one: the split
+        # workspace was sized at init, so nothing needs allocating.
         q_s = qs[0].clone()
         out_s = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
         graph = torch.cuda.CUDAGraph()
@@ -96,6 +92,13 @@ def test_decode_replayed_from_a_graph():
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.graph(graph, stream=side):
             hs.hisparse_sparse_mla_decode(pool, None, B, H, k, 0, q_s, locs, scale, out_s)
+        torch.cuda.synchronize()
+
+        want = []
+        for q in qs:  # eager calls on the same pool
+            o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+            hs.hisparse_sparse_mla_decode(pool, None, B, H, k, 0, q, locs, scale, o)
+            want.append(o)
         torch.cuda.synchronize()
 
         for rep in range(2):
@@ -112,8 +115,8 @@ def test_decode_replayed_from_a_graph():
 
 
 def test_overlapped_layers_replayed_from_a_graph():
-    """Plan plus the overlapped per-layer copy and decode (two pool streams
-    forked from the caller's stream by events and joined back) captured once
+    """Plan plus the overlapped per-layer copy and decode (every launch on
+    the caller's stream) captured once, before the pool has run anything,
     and replayed: each replay equals the eager sequential order bit for bit
     (row IDs, state, counters, device pools, every layer's output)."""
     print("[graph] overlapped layers", flush=True)
@@ -122,8 +125,8 @@ def test_overlapped_layers_replayed_from_a_graph():
     w = synth("ovlgraph", 91, R=B, S=256, k=128, steps=5, n0=[3000 + 700 * b for b in range(B)],
               L=L, grow=1, keep=80, recent=16, recent_window=64)
     bufs = make_host_pools(w, kind="mla")
-    seq = Pair(w, bufs, with_oracle=False)
-    ovl = Pair(w, bufs, with_oracle=False)
+    seq = Pair(w, bufs, with_oracle=False, max_heads=H)
+    ovl = Pair(w, bufs, with_oracle=False, max_heads=H)
     try:
         qs = [make_queries(w.B, H, seed=20 + l, device="cuda") for l in range(L)]
         outs_s = [torch.empty((w.B, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
@@ -157,13 +160,8 @@ def test_overlapped_layers_replayed_from_a_graph():
                 assert torch.equal(seq.dev_pools[l], ovl.dev_pools[l]), "pool %d, step %d" % (l, step)
                 assert torch.equal(outs_s[l], outs_o[l]), "output of layer %d, step %d" % (l, step)
 
-        # step 0 eagerly on both sides: it also creates the pool's streams,
-        # events and decode workspace, which capture cannot
-        sequential(0)
-        ovl.pre_step_writes(0)
-        overlapped()
-        compare(0)
-
+        # captured before the pool's first call: the decode workspace was
+        # sized at init, so the first overlapped call allocates nothing
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -171,7 +169,7 @@ def test_overlapped_layers_replayed_from_a_graph():
             overlapped()
         torch.cuda.synchronize()
 
-        for step in range(1, w.steps):
+        for step in range(w.steps):
             sequential(step)
             ovl.pre_step_writes(step)
             topk_s.copy_(ovl.topk[step])

@@ -38,8 +38,8 @@ def test_overlapped_layers_match_sequential(B, L, corrupt):
         locs[rng.random(locs.shape) < 0.04] = -3
         locs[rng.random(locs.shape) < 0.04] = w.host_pool_rows + 7
     bufs = make_host_pools(w, kind="mla")
-    seq = Pair(w, bufs, with_oracle=False)
-    ovl = Pair(w, bufs)
+    seq = Pair(w, bufs, with_oracle=False, max_heads=H)
+    ovl = Pair(w, bufs, max_heads=H)
     try:
         qs = [make_queries(w.B, H, seed=10 + l, device="cuda") for l in range(L)]
         for step in range(w.steps):
@@ -88,7 +88,7 @@ def test_overlapped_rejects_bad_layer_before_enqueueing():
     print("[overlap] bad last layer", flush=True)
     L, H, B = 3, 32, 4
     w = synth("ovl_bad", 91, R=B, S=256, k=128, steps=1, n0=[3000, 3500, 4000, 4500], L=L)
-    pair = Pair(w, make_host_pools(w, kind="mla"), with_oracle=False)
+    pair = Pair(w, make_host_pools(w, kind="mla"), with_oracle=False, max_heads=H)
     try:
         pair.pre_step_writes(0)
         hs.hisparse_resolve_plan(pair.pool, None, w.B, w.k, pair.req_idx, pair.topk[0], pair.seq[0],

@@ -205,6 +205,48 @@ def test_host_side_errors():
         pair.close()
 
 
+def test_copy_batch_must_match_the_plan():
+    """A copy replays the compact plan of the last plan call: before any plan,
+    or with a batch other than the plan's, the copy entry points refuse
+    (EINVAL) instead of replaying rows of an older plan; so does a decode of
+    more heads than the pool's max_heads or more rows than its max_batch.
+    The pool then runs a normal step, checked against the oracle."""
+    import ctypes
+    print("[copy batch check]", flush=True)
+    w = synth("cbatch", 29, R=4, S=64, k=8, steps=2, n0=[500, 700, 900, 300])
+    pair = Pair(w, make_host_pools(w), mode="split", max_heads=16)
+    lib = hs.load_library()
+    h = ctypes.c_void_p(pair.pool.handle)
+    try:
+        rc = lib.hisparse_gather_copy(h, None, w.B, 0, 1, None)
+        assert rc == -1 and "no plan" in hs.hisparse_last_error()
+        dst, src = pair.gpu_step(0)          # plan of batch w.B, then its copy
+        o = pair.oracle_step(0, dst, src)
+        rc = lib.hisparse_gather_copy(h, None, w.B - 1, 0, 1, None)
+        assert rc == -1 and "differs" in hs.hisparse_last_error()
+        rc = lib.hisparse_gather_copy_step(h, None, 0, w.B + 0, 0, 1, None)
+        assert rc == 0, hs.hisparse_last_error()   # same batch: a valid replay
+        rc = lib.hisparse_gather_copy_step(h, None, 0, 2, 0, 1, None)
+        assert rc == -1 and "differs" in hs.hisparse_last_error()
+        q = torch.zeros((w.B, 32, 576), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((w.B, 32, 512), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(hs.HisparseError, match="max_heads"):
+            hs.hisparse_sparse_mla_decode(pair.pool, None, w.B, 32, w.k, 0, q, pair.out, 1.0, out)
+        rc = lib.hisparse_sparse_mla_decode(h, None, w.B + 1, 16, w.k, 0,
+                                            ctypes.c_void_p(q.data_ptr()),
+                                            ctypes.c_void_p(pair.out.data_ptr()), ctypes.c_float(1.0),
+                                            ctypes.c_void_p(out.data_ptr()))
+        assert rc == -1 and "max_batch" in hs.hisparse_last_error()
+        torch.cuda.synchronize()
+        pair.compare_step(0, o)
+        dst, src = pair.gpu_step(1)
+        o = pair.oracle_step(1, dst, src)
+        torch.cuda.synchronize()
+        pair.compare_step(1, o)
+    finally:
+        pair.close()
+
+
 def test_pool_holds_its_buffers():
     """The library keeps raw pointers to the device pools and host buffers,
     so the binding's pool object keeps them alive until it is destroyed: a

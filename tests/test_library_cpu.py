@@ -37,11 +37,57 @@ def test_library_loads_and_exports_every_symbol():
     assert hs.hisparse_last_error() == ""
 
 
+def _offload_bundle_targets(data: bytes):
+    """Target IDs of every clang offload bundle embedded in a shared library
+    (magic, entry count, then per entry: offset, size, ID length, ID)."""
+    import struct
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    ids, pos = [], 0
+    while True:
+        i = data.find(magic, pos)
+        if i < 0:
+            return ids
+        j = i + len(magic)
+        n, = struct.unpack_from("<Q", data, j)
+        j += 8
+        assert 0 < n < 16, "malformed bundle header at %d" % i
+        for _ in range(n):
+            _off, _size, idlen = struct.unpack_from("<QQQ", data, j)
+            j += 24
+            ids.append(data[j:j + idlen].decode("ascii"))
+            j += idlen
+        pos = i + 1
+
+
 def test_library_is_gfx950_code_object():
+    """Every offload bundle in the library holds host code and gfx950 device
+    code only: no other GPU target is built."""
     import hierarchical_sparse_attention_hisparse_amd as hs
     data = open(hs.library_path(), "rb").read()
-    assert b"gfx950" in data
-    assert b"sm_" not in data[:0]  # nothing NVIDIA-specific is built
+    ids = _offload_bundle_targets(data)
+    device = [t for t in ids if not t.startswith("host-")]
+    assert device, "no device code object in the library"
+    assert set(device) == {"hipv4-amdgcn-amd-amdhsa--gfx950"}, ids
+    assert all(t.startswith("host-x86_64") for t in ids if t.startswith("host-"))
+
+
+def test_host_alloc_refuses_more_than_the_available_ram():
+    """hisparse_host_alloc checks the request against 95% of MemAvailable
+    before pinning anything: a request far beyond the host's memory is
+    refused with ENOMEM and a message naming the limit (no GPU needed)."""
+    import hierarchical_sparse_attention_hisparse_amd as hs
+    lib = hs.load_library()
+    out = ctypes.c_void_p(1)
+    rc = lib.hisparse_host_alloc(ctypes.c_size_t(1 << 60), ctypes.byref(out))
+    msg = hs.hisparse_last_error()
+    assert rc == -2 and "MemAvailable" in msg and out.value is None, (rc, msg)
+    avail = 0
+    for line in open("/proc/meminfo"):
+        if line.startswith("MemAvailable:"):
+            avail = int(line.split()[1]) * 1024
+    # just above the limit: refused by the same check
+    rc = lib.hisparse_host_alloc(ctypes.c_size_t(int(0.96 * avail)), ctypes.byref(out))
+    assert rc == -2 and "MemAvailable" in hs.hisparse_last_error()
 
 
 def test_binding_rejects_bad_arguments_before_any_device_call():
