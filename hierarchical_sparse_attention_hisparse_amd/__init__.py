@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     hisparse_resolve_plan,
     hisparse_resolve_steps,
     hisparse_sparse_mla_decode,
+    hisparse_sparse_mla_decode_noalloc,
     library_path,
     load_library,
 )

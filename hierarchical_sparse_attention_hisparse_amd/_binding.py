@@ -101,6 +101,9 @@ def load_library():
     lib.hisparse_sparse_mla_decode.restype = I
     lib.hisparse_sparse_mla_decode.argtypes = [V, V, I32, I32, I32, I32, V, V,
                                                ctypes.c_float, V]
+    lib.hisparse_sparse_mla_decode_noalloc.restype = I
+    lib.hisparse_sparse_mla_decode_noalloc.argtypes = [V, I32, I32, I32, V, I64, I32, V, V,
+                                                       ctypes.c_float, V]
     _lib = lib
     return lib
 
@@ -375,6 +378,24 @@ def hisparse_sparse_mla_decode(pool, stream, batch, heads, top_k, layer, q_bf16,
                                                         batch, heads, top_k, layer, qp, lp,
                                                         ctypes.c_float(softmax_scale), op),
               "hisparse_sparse_mla_decode")
+
+
+def hisparse_sparse_mla_decode_noalloc(stream, batch, heads, top_k, device_pool, q_bf16,
+                                       device_buffer_locs, softmax_scale, out_bf16):
+    """The decode without a pool: ``device_pool`` is one layer's uint8 cuda
+    tensor [rows, row_bytes]; nothing is allocated (static split workspace)."""
+    import torch
+    if device_pool.dim() != 2:
+        raise ValueError("device_pool must be [rows, row_bytes]")
+    dev = device_pool.get_device()
+    pp = _dev(device_pool, torch.uint8, None, "device_pool", device=dev)
+    qp = _dev(q_bf16, torch.bfloat16, (batch, heads, 576), "q_bf16", device=dev)
+    lp = _dev(device_buffer_locs, torch.int32, (batch, top_k), "device_buffer_locs", device=dev)
+    op = _dev(out_bf16, torch.bfloat16, (batch, heads, 512), "out_bf16", device=dev)
+    _check_rc(load_library().hisparse_sparse_mla_decode_noalloc(
+        _stream_handle(stream), batch, heads, top_k, pp, int(device_pool.shape[0]),
+        int(device_pool.shape[1]), qp, lp, ctypes.c_float(softmax_scale), op),
+        "hisparse_sparse_mla_decode_noalloc")
 
 
 def hisparse_decode_layers_overlapped(pool, stream, batch, heads, top_k, q_per_layer,

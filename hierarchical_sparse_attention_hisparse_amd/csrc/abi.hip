@@ -9,6 +9,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/hisparse.h"
 #include "common.h"
 #include "kernels.h"
@@ -195,6 +197,45 @@ int launch_copy(hisparse_pool* pool, hipStream_t stream, int32_t batch, int32_t 
   c.layer_begin = lb;
   hipError_t e = launch_gather_copy(c, batch, le - lb, stream);
   if (e != hipSuccess) return hip_fail(e, "gather copy kernel launch");
+  return HISPARSE_OK;
+}
+
+}  // namespace
+
+// Split partials of hisparse_sparse_mla_decode_noalloc, for callers that
+// cannot allocate: a file-scope device array, one copy per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, once per device (noalloc_scratch below), and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[(size_t)kNoAllocDecodeUnits * kDecodeUnitBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+
+// The current device's address of `scratch` (looked up on the device's first
+// call, which also sets the decode kernels' LDS limit there).  No allocation.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HISPARSE_EUNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(HISPARSE_EHIP, "hipGetSymbolAddress of the decode scratch on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    if ((e = prepare_sparse_mla_decode()) != hipSuccess) return hip_fail(e, "decode kernel set-up");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return HISPARSE_OK;
 }
 
@@ -755,6 +796,61 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t
                        l > 0 ? out_bf16[l - 1] : nullptr, !last);
     if (rc != HISPARSE_OK) return rc;
   }
+  return ok();
+}
+
+int hisparse_sparse_mla_decode_noalloc(void* stream, int32_t batch, int32_t heads, int32_t top_k,
+                                       const void* device_pool, int64_t device_pool_rows,
+                                       int32_t row_bytes, const void* q_bf16,
+                                       const int32_t* device_buffer_locs, float softmax_scale,
+                                       void* out_bf16) {
+  if (batch < 0) return fail(HISPARSE_EINVAL, "batch %d < 0", batch);
+  if (heads <= 0 || heads % 16 != 0)
+    return fail(HISPARSE_EUNSUPPORTED, "heads %d must be a positive multiple of 16", heads);
+  if (top_k < 0 || top_k > kMaxTopK)
+    return fail(HISPARSE_EINVAL, "top_k %d outside [0, %d]", top_k, kMaxTopK);
+  if (row_bytes < 656 || row_bytes % 16 != 0)
+    return fail(HISPARSE_EUNSUPPORTED, "row_bytes %d must be a multiple of 16 and >= 656", row_bytes);
+  if (device_pool_rows < 0 || device_pool_rows > INT32_MAX)
+    return fail(HISPARSE_EINVAL, "device_pool_rows outside [0, 2^31)");
+  const int HG = (heads + 127) / 128;
+  if ((int64_t)batch * HG > kNoAllocDecodeUnits)
+    return fail(HISPARSE_EUNSUPPORTED,
+                "batch %d x ceil(heads/128) = %lld exceeds the %d units of the static split "
+                "workspace (%zu bytes)",
+                batch, (long long)batch * HG, kNoAllocDecodeUnits,
+                (size_t)kNoAllocDecodeUnits * kDecodeUnitBytes);
+  if (batch == 0) return ok();
+  if (!device_pool || !q_bf16 || !out_bf16 || (top_k > 0 && !device_buffer_locs))
+    return fail(HISPARSE_EINVAL, "device_pool, q_bf16, out_bf16 and device_buffer_locs must not be NULL");
+  if (!aligned(device_pool, 16) || !aligned(q_bf16, 16) || !aligned(out_bf16, 8) ||
+      !aligned(device_buffer_locs, 4))
+    return fail(HISPARSE_EINVAL,
+                "device_pool and q_bf16 must be 16-byte, out_bf16 8-byte and locs 4-byte aligned");
+  const int splits = decode_splits(batch, heads, top_k);
+  const size_t one = decode_workspace_bytes(batch, heads, splits);
+  if (one > (size_t)kNoAllocDecodeUnits * kDecodeUnitBytes)  // implied by the unit check above
+    return fail(HISPARSE_EUNSUPPORTED, "decode workspace of %zu bytes exceeds the static one", one);
+  void* ws = nullptr;
+  int rc = noalloc_scratch(&ws);
+  if (rc != HISPARSE_OK) return rc;
+  const size_t entries = one / (512 * sizeof(uint16_t) + 2 * sizeof(float));
+  DecodeParams d = {};
+  d.splits = splits;
+  d.part_o = (uint16_t*)ws;
+  d.part_ml = (float*)(d.part_o + entries * 512);
+  d.pool = (const unsigned char*)device_pool;
+  d.pool_rows = device_pool_rows;
+  d.row_bytes = row_bytes;
+  d.heads = heads;
+  d.k = top_k;
+  d.batch = batch;
+  d.scale = softmax_scale;
+  d.q = (const uint16_t*)q_bf16;
+  d.locs = device_buffer_locs;
+  d.out = (uint16_t*)out_bf16;
+  hipError_t e = launch_sparse_mla_decode(d, batch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse-MLA decode kernel launch");
   return ok();
 }
 

@@ -38,6 +38,12 @@ constexpr int kInvalidateLdsRows = 8192;
 
 // Decode: at most this many key splits per (batch row, head group).
 constexpr int kMaxDecodeSplits = 16;
+// Decode split workspace per (batch row, 128-head group, split): bf16 partial
+// O [128][512] and fp32 (reference, denominator) [128][2].
+constexpr size_t kDecodeUnitBytes = 128 * (512 * sizeof(uint16_t) + 2 * sizeof(float));
+// The allocation-free decode keeps its split partials in a static device
+// array of this many units (33.8 MB): any batch * ceil(heads / 128) <= 256.
+constexpr int kNoAllocDecodeUnits = 256;
 
 __host__ __device__ inline int next_pow2(int v) {
   int p = 1;

@@ -75,6 +75,8 @@ constexpr int kHeadTiles = kHeadsPerGroup / 16;    // 8
 constexpr int kDimTilesPerWave = kLat / 16 / kDecWaves;  // 8: O dims 128w..128w+127
 constexpr size_t kOffP = kOffQRope + (size_t)kHeadsPerGroup * kQRopeStrideBytes;  // P^T fragments
 constexpr size_t kPBytes = (size_t)kHeadTiles * 64 * 16;
+static_assert(kDecodeUnitBytes == kHeadsPerGroup * (kLat * sizeof(uint16_t) + 2 * sizeof(float)),
+              "split workspace unit");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -363,6 +363,32 @@ int hisparse_decode_layers_overlapped(hisparse_pool* pool, void* stream, int32_t
                                       const int32_t* device_buffer_locs, float softmax_scale,
                                       void* const* out_bf16, uint64_t* stats);
 
+/*
+ * hisparse_sparse_mla_decode_noalloc -- hisparse_sparse_mla_decode without a
+ * pool and without allocating anything, for callers that cannot allocate
+ * device memory: code under stream capture set up before any pool exists,
+ * serving loops and harnesses that forbid hipMalloc.  Same attention, same
+ * kernels and key splits, so its output equals hisparse_sparse_mla_decode's
+ * bit for bit on the same rows.
+ *   device_pool       device: one layer's rows, device_pool_rows rows of
+ *                     row_bytes (>= 656, a multiple of 16), 16-byte aligned
+ *   q_bf16, device_buffer_locs, softmax_scale, out_bf16: as in
+ *                     hisparse_sparse_mla_decode
+ * The split partials live in a static device array of the library (33.8 MB,
+ * held on every GPU the library runs on until the process ends), so
+ * batch * ceil(heads / 128) must not exceed 256 (EUNSUPPORTED otherwise);
+ * heads is a multiple of 16 and top_k <= 4096.  The array's address is
+ * looked up on the first call on each device.  Every call on one GPU shares
+ * that array: calls that overlap in time on one GPU (different streams, or
+ * different threads) race on it and must be ordered by the caller.  Errors:
+ * EINVAL, EUNSUPPORTED, EHIP.
+ */
+int hisparse_sparse_mla_decode_noalloc(void* stream, int32_t batch, int32_t heads, int32_t top_k,
+                                       const void* device_pool, int64_t device_pool_rows,
+                                       int32_t row_bytes, const void* q_bf16,
+                                       const int32_t* device_buffer_locs, float softmax_scale,
+                                       void* out_bf16);
+
 /* Free the pool's workspace and the pool.  NULL is a no-op.  The caller must
  * make sure no work that uses the pool is still queued. */
 void hisparse_destroy_pool(hisparse_pool* pool);
