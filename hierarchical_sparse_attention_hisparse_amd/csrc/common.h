@@ -16,8 +16,8 @@ constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxSlots = 16384;
 constexpr size_t kLdsBudget = 160 * 1024;             // bytes of LDS per CU (gfx950)
-constexpr int kVictimRounds = 4;                      // min-extraction rounds before
-                                                      // the full sort fallback
+constexpr int kMaxRankBins = 32;                      // consecutive keys ranked per window
+constexpr int kMaxRankWindows = 4;                    // windows before the full-sort fallback
 
 // Copy kernel shape.
 constexpr int kCopyThreads = 256;
@@ -59,13 +59,16 @@ __host__ __device__ inline int ilog2(int v) {
 
 // Byte offsets of the resolver's dynamic LDS carve-up for S slots and top-k k.
 // The open-addressing table and the per-entry hit slots are dead once the
-// misses are listed, so the fallback victim sort reuses their bytes.
-constexpr int kResolveScratchInts = 160 + 32 * kVictimRounds;
+// slots have probed the table, so the victim ranking's per-key slot bitmaps
+// (and their word prefixes) and the fallback victim sort reuse their bytes.
+constexpr int kResolveScratchInts = 176;
 
 struct ResolveLds {
-  int hash_size;   // cells of the open-addressing table (power of two >= 2k)
+  int hash_size;   // cells of the table (power of two >= 2k)
   int sort_size;   // power of two >= S (fallback sort)
-  size_t off_hash, off_ehit, off_sort;
+  int words;       // 64-bit words of one slot bitmap: ceil(S / 64)
+  int bins;        // keys ranked per window (<= kMaxRankBins), 0 = sort only
+  size_t off_hash, off_hidx, off_ehit, off_sort, off_bits, off_wpre;
   size_t off_etok, off_mentry, off_mhost, off_victim, off_scratch;
   size_t total;
 };
@@ -86,12 +89,24 @@ __host__ __device__ inline ResolveLds resolve_lds_layout_f(int S, int k, int fac
   L.hash_size = next_pow2(factor * k < 64 ? 64 : factor * k);
   L.sort_size = next_pow2(S);
   size_t o = 0;
-  L.off_hash = o;
-  L.off_ehit = align16(L.off_hash + 8 * (size_t)L.hash_size);
+  L.off_hash = o;                                               // int32 positions
+  L.off_hidx = align16(L.off_hash + 4 * (size_t)L.hash_size);   // uint16 top-k indices
+  L.off_ehit = align16(L.off_hidx + 2 * (size_t)L.hash_size);
   const size_t end_hash = align16(L.off_ehit + 4 * (size_t)k);
   L.off_sort = o;
   const size_t end_sort = align16(L.off_sort + 8 * (size_t)L.sort_size);
   o = end_hash > end_sort ? end_hash : end_sort;
+  // Ranking bitmaps: the larger dead piece of the region above, either the
+  // table or what lies past the per-entry hit slots.  Per word of slots:
+  // bins + 1 (a padding column) 64-bit bitmap words and 32-bit prefixes.
+  L.words = (S + 63) / 64;
+  const size_t per_col = 12 * (size_t)L.words;
+  const size_t piece1 = L.off_ehit, piece2 = o - end_hash;
+  const size_t piece = piece1 > piece2 ? piece1 : piece2;
+  const size_t nb = piece / per_col;  // columns, one of them padding
+  L.bins = nb < 2 ? 0 : (nb - 1 > (size_t)kMaxRankBins ? kMaxRankBins : (int)(nb - 1));
+  L.off_bits = piece1 >= piece2 ? 0 : end_hash;
+  L.off_wpre = L.off_bits + 8 * (size_t)L.words * (L.bins + 1);
   L.off_etok = o;    o = align16(o + 4 * (size_t)k);
   L.off_mentry = o;  o = align16(o + 4 * (size_t)k);
   L.off_mhost = o;   o = align16(o + 4 * (size_t)k);

@@ -2,29 +2,29 @@
 //
 // One workgroup of 1024 threads (16 wavefronts) per batch row.  Thread t owns
 // a contiguous run of SPT slots and a contiguous run of KPT top-k entries, so
-// "ascending slot" and "ascending top-k index" are thread order and every
-// rank below is a block-wide exclusive scan.  Slot tokens and stamps stay in
-// registers; LDS holds an open-addressing table of the pending positions
-// (one 64-bit word per cell: position << 32 | top-k index), the per-entry hit
-// slot, the miss and victim lists, and per-wave partials.  Steps:
+// "ascending slot" and "ascending top-k index" are thread order.  Slot tokens
+// and stamps stay in registers; LDS holds an open-addressing table of the
+// pending positions (one 64-bit word per cell: position << 32 | top-k index),
+// the per-entry hit slot, the miss list, the victim ranking's bitmaps and
+// per-wave partials.  Steps:
 //   1. validity and the resident short-circuit; pending positions are
 //      inserted into the table;
 //   2. each slot holding a pending position marks that entry's hit slot (the
 //      lowest slot if the map was corrupted into duplicates);
-//   3. hits get their row ID and a refreshed stamp; misses are listed in
-//      ascending top-k index with their host rows (loaded as soon as each
-//      miss is known); a slot learns it is a hit slot from its entry;
-//   4. victims: rounds of block-wide minimum over the candidates' (occupied,
-//      stamp) keys, each round taking the slots of the minimum key in slot
-//      order; if a few rounds do not cover every miss, a bitonic LDS sort of
-//      the remaining candidates finishes the ranking;
+//   3. hits get their row ID and a refreshed stamp; misses load their host
+//      rows; a slot learns it is a hit slot from its entry;
+//   4. the misses are listed in ascending top-k index; victims are ranked in
+//      (occupied, stamp, slot) order by windows of consecutive keys: one
+//      slot bitmap per key, popcount prefixes over each bitmap's words, and
+//      a candidate's exact rank from those (three barriers per window; keys
+//      spread over more windows fall back to a bitonic sort);
 //   5. the j-th miss takes the j-th victim: token, stamp, row ID and one
 //      (host row, device row) entry of the compact miss plan;
 //   6. (COPY instances) the workgroup copies its own misses from the pinned
 //      host pools into every layer, one wavefront per row, so each request's
 //      copy starts as soon as its plan exists and no second launch is needed;
-//      each wavefront's first rows are loaded before step 4, so the host link
-//      is busy while the victims are ranked.
+//      each wavefront's first rows are loaded before the ranks are known, so
+//      the host link is busy while the victims are ranked.
 // Resolution order and phases: "vLLM HiSparse 本地 KV 卸载架构" (hot-row lookup
 // and LRU) and "vLLM Hybrid HiSparse 源码实现分析" section 7.2; fast path
 // (seq_len <= S: slot == position, nothing moves): the per-step flow of the
@@ -37,8 +37,6 @@
 namespace hisparse {
 
 namespace {
-
-constexpr uint64_t kEmptyCell = ~0ull;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4 gu4;  // 16 bytes of global memory
@@ -169,32 +167,29 @@ __device__ inline int block_exscan_small(int c, int* buf, int* total) {
   return base + pre;
 }
 
-// Block-wide minimum of victim keys with one barrier; `buf` holds 16 u64 for
-// this call site.
-__device__ inline uint64_t block_min_key(uint64_t v, uint64_t* buf) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const uint64_t wm = wave_min_key(v);
-  if (lane == 0) buf[wid] = wm;
-  lds_barrier();
-  return wave_min_key(lane < kResolveWaves ? buf[lane] : ~0ull);  // lane w: wave w's minimum
-}
-
 __device__ inline uint32_t hash_pos(int t, int shift) {
   return ((uint32_t)t * 2654435761u) >> shift;  // Knuth multiplicative hash
 }
 
 constexpr int bits_for(int v) { return v <= 1 ? 1 : 1 + bits_for(v >> 1); }
 
-// Scratch buffers (16 entries each) of the call sites, in ints.
+// A host row as int32 for the fused copy's LDS list: host pools hold fewer
+// than 2^31 rows (checked at init), so a row outside [0, 2^31) becomes -1,
+// out of range either way.
+__device__ inline int32_t host_row32(int64_t h) { return (h >= 0 && h <= INT_MAX) ? (int32_t)h : -1; }
+
+// Scratch buffers of the call sites, in ints: per-wave partials (16 each)
+// and the window's candidate count per key.
 enum : int {
   kScrFast = 0,
   kScrMiss = 16,
   kScrStats = 32,        // 3 x 16
-  kScrRoundScan = 80,    // kVictimRounds x 16
-  kScrRoundMin = 160,    // kVictimRounds x 16 u64 (= 32 ints each), 8-byte aligned
-  kScrInts = 160 + 32 * kVictimRounds
+  kScrMin = 80,          // 2 x 16 u64 (= 64 ints), 8-byte aligned: double-buffered per window
+  kScrBtot = 144,        // kMaxRankBins
+  kScrInts = 176
 };
 static_assert(kScrInts == kResolveScratchInts, "scratch layout");
+static_assert(kScrBtot + kMaxRankBins <= kScrInts, "scratch layout");
 
 // COPY: the workgroup also copies its misses into p.copy_layers layers.
 // VEC: each thread's slot-state run is loaded as vectors.
@@ -234,7 +229,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   }
 
   const int64_t n = (int64_t)nraw < p.max_seq_len ? (int64_t)nraw : p.max_seq_len;
-  const int32_t c = (int32_t)((uint32_t)p.clk[r] + 1u);
   int32_t* st = p.st + (int64_t)r * S;
   int32_t* lru = p.lru + (int64_t)r * S;
   const int rowbase = r * S;
@@ -242,6 +236,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int* scr = (int*)(smem + L.off_scratch);
 
   if (nraw <= S) {  // fast path: slot == position, nothing copied
+    const int32_t c = (int32_t)((uint32_t)p.clk[r] + 1u);
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -287,6 +282,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
 
+  // The request's clock, through a vector load (a zero the compiler cannot
+  // see through makes its address a vector one): the barriers wait for every
+  // scalar load in flight, so as a scalar load it would hold the first one
+  // for a second dependent round trip.  It is first used at the end.
+  int vzero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+  const int32_t clk_now = p.clk[r + vzero];
+
   // Block-table entries of this thread's positions, at in-range indices,
   // issued with the slot-state loads so that both round trips overlap.
   int pgs[KPT];
@@ -300,19 +303,27 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
 
-  uint64_t* H = (uint64_t*)(smem + L.off_hash);
+  // Table of the pending positions: linear probing over 32-bit cells (a
+  // position, -1 = empty), with the top-k index of each cell in a parallel
+  // 16-bit array.  Inserts take the first free cell from the position's
+  // hash with one compare-and-swap per step; probes read the cells in
+  // aligned groups of four (16 bytes), stop at the first match or free cell,
+  // and read the matched cell's index once, after their loop.  Cells are
+  // never freed within a call, so every cell between a position's hash and
+  // its own is taken.
+  int32_t* Hc = (int32_t*)(smem + L.off_hash);
+  uint16_t* Hi = (uint16_t*)(smem + L.off_hidx);
   int32_t* e_hit = (int32_t*)(smem + L.off_ehit);
   int32_t* e_tok = (int32_t*)(smem + L.off_etok);
   int32_t* m_entry = (int32_t*)(smem + L.off_mentry);
   int32_t* victim = (int32_t*)(smem + L.off_victim);
-  // Host row of the j-th miss.  Host pools hold fewer than 2^31 rows (checked
-  // at init), so a row outside [0, 2^31) is kept as -1: out of range either way.
+  // Host row of the j-th miss for the fused copy (see host_row32).
   int32_t* m_h = (int32_t*)(smem + L.off_mhost);
   uint64_t* s_sort = (uint64_t*)(smem + L.off_sort);
   const int HS = L.hash_size;
   const int hshift = 32 - ilog2(HS);
 
-  for (int x = tid; x < HS; x += kResolveThreads) H[x] = kEmptyCell;
+  for (int x = tid; x < HS / 4; x += kResolveThreads) ((i32x4*)Hc)[x] = i32x4{-1, -1, -1, -1};
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (i0 + j < k) e_hit[i0 + j] = INT_MAX;
@@ -344,167 +355,311 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
     pend |= 1u << j;
     e_tok[i] = t;
-    const uint64_t cell = ((uint64_t)(uint32_t)t << 32) | (uint32_t)i;
     uint32_t h = hash_pos(t, hshift);
     while (true) {
-      const uint64_t prev = atomicCAS((unsigned long long*)&H[h], kEmptyCell, cell);
-      if (prev == kEmptyCell || (int)(prev >> 32) == t) break;  // inserted, or a repeat
+      const int prev = atomicCAS(&Hc[h], -1, t);
+      if (prev == -1) {
+        Hi[h] = (uint16_t)i;
+        break;
+      }
+      if (prev == t) break;  // a repeat
       h = (h + 1) & (HS - 1);
     }
   }
   lds_barrier();
 
   // Step 2: probe the table with every slot's token; the SPT probes of a
-  // thread advance together so a wavefront waits for its longest chain once.
+  // thread advance together (their first groups read back to back), so a
+  // wavefront waits for its longest chain once.  Cells of a group below the
+  // probe's start are skipped (-2: neither free nor a position).
   int hidx[SPT];  // top-k index of the pending entry this slot's token matches, or -1
   {
-    uint32_t hh[SPT];
-    uint64_t hv[SPT];
+    uint32_t g[SPT], o[SPT];
+    i32x4 v[SPT];
+    int hcell[SPT];  // table cell holding this slot's token, or -1
     unsigned live = 0;
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int tok = sr[j];
-      const bool ok = (s0 + j < S) && tok >= 0 && (int64_t)tok < n;
-      hh[j] = hash_pos(tok, hshift);
-      hv[j] = ok ? H[hh[j]] : kEmptyCell;
-      if (ok) live |= 1u << j;
+      if ((s0 + j < S) && tok >= 0 && (int64_t)tok < n) live |= 1u << j;
+      const uint32_t h = hash_pos(tok, hshift);  // in range for any token
+      g[j] = h >> 2;
+      o[j] = h & 3;
+      v[j] = ((const i32x4*)Hc)[g[j]];
+      hcell[j] = -1;
     }
     while (true) {
       unsigned next = 0;
 #pragma unroll
-      for (int j = 0; j < SPT; ++j)
-        if ((live & (1u << j)) && hv[j] != kEmptyCell && (int)(hv[j] >> 32) != sr[j])
-          next |= 1u << j;
+      for (int j = 0; j < SPT; ++j) {
+        const int tok = sr[j];
+        const int c0 = o[j] <= 0 ? v[j].x : -2, c1 = o[j] <= 1 ? v[j].y : -2;
+        const int c2 = o[j] <= 2 ? v[j].z : -2, c3 = v[j].w;
+        const int q = c0 == tok ? 0 : c1 == tok ? 1 : c2 == tok ? 2 : c3 == tok ? 3 : 4;
+        const bool fr = (c0 == -1) | (c1 == -1) | (c2 == -1) | (c3 == -1);
+        const bool lj = (live >> j) & 1u;
+        hcell[j] = (lj && q < 4) ? (int)(4 * g[j]) + q : hcell[j];
+        next |= (lj && q == 4 && !fr) ? 1u << j : 0u;  // no match, no free cell: next group
+      }
       if (next == 0) break;
+      live = next;
 #pragma unroll
-      for (int j = 0; j < SPT; ++j)
-        if (next & (1u << j)) {
-          hh[j] = (hh[j] + 1) & (HS - 1);
-          hv[j] = H[hh[j]];
-        }
+      for (int j = 0; j < SPT; ++j) {
+        const bool nj = (next >> j) & 1u;
+        g[j] = nj ? (g[j] + 1) & (HS / 4 - 1) : g[j];
+        o[j] = nj ? 0 : o[j];
+        v[j] = ((const i32x4*)Hc)[g[j]];
+      }
     }
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      hidx[j] = ((live & (1u << j)) && hv[j] != kEmptyCell) ? (int)(uint32_t)hv[j] : -1;
+    for (int j = 0; j < SPT; ++j) hidx[j] = hcell[j] >= 0 ? (int)Hi[hcell[j] >= 0 ? hcell[j] : 0] : -1;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
       if (hidx[j] >= 0) atomicMin(&e_hit[hidx[j]], s0 + j);
-    }
   }
   lds_barrier();
 
-  // Step 3: hits and the ordered miss list.  A miss's host row is loaded as
-  // soon as the miss is known; it travels with the list.
+  // Step 3: hits and misses.  An entry's hit slot is the one its e_hit
+  // names; a miss's host row is loaded as soon as the miss is known and used
+  // only at the end (every lane loads, hits and invalid entries the row's
+  // first location, so the load sits in no branch that would wait for it).
+  // A slot is a hit slot if the entry its token matched names it.  Then the per-wave partials: counters, misses, and the
+  // smallest victim key (occupied << 32 | biased stamp) among the
+  // candidates (slots that are not hit slots); and the ranking bitmaps of
+  // the first window are cleared (the table is dead).
   const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
   int n_hit = 0, my_miss = 0;
   unsigned missbits = 0;
-  int32_t hm[KPT];
+  int sh[KPT];
+  unsigned hitbits = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    hm[j] = -1;
-    if (!(pend & (1u << j))) continue;
-    const int i = i0 + j;
-    const int s = e_hit[i];
-    if (s != INT_MAX) {
-      outb[i] = rowbase + s;  // the slot's owner refreshes its stamp
-      ++n_hit;
-    } else {
-      missbits |= 1u << j;
-      ++my_miss;
-      const int64_t h = locr[tr[j]];
-      hm[j] = (h >= 0 && h <= INT_MAX) ? (int32_t)h : -1;
-    }
+    sh[j] = k > 0 ? e_hit[min(i0 + j, k - 1)] : INT_MAX;
+    const unsigned pj = (pend >> j) & 1u;
+    const unsigned mj = pj & (sh[j] == INT_MAX ? 1u : 0u);
+    missbits |= mj << j;
+    hitbits |= (pj & (mj ^ 1u)) << j;
+    my_miss += (int)mj;
   }
-  {
-    const int a0 = wave_sum_small<bits_for(KPT)>(n_hit);
-    const int a1 = wave_sum_small<bits_for(KPT)>(n_res);
-    const int a2 = wave_sum_small<bits_for(KPT)>(n_trip);
-    if (lane == 0) {
-      scr[kScrStats + wid] = a0;
-      scr[kScrStats + 16 + wid] = a1;
-      scr[kScrStats + 32 + wid] = a2;
-    }
-  }
-  int m_total;
-  int mpos = block_exscan_small<bits_for(KPT)>(my_miss, scr + kScrMiss, &m_total);
-  // Slots: the hit slot of an entry is the one that entry's e_hit names.
+  n_hit = __popc(hitbits);
+  // The misses' host rows: one unconditional load per entry (the row's first
+  // location for the others), so no branch joins wait for them.
+  int64_t hraw[KPT];  // host row of each miss (entries that are not misses: unused)
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) hraw[j] = locr[tr[j] & -(int)((missbits >> j) & 1u)];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (hitbits & (1u << j)) outb[i0 + j] = rowbase + sh[j];  // the slot's owner refreshes its stamp
   unsigned hitm = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
     if (hidx[j] >= 0 && e_hit[hidx[j]] == s0 + j) hitm |= 1u << j;
-
-  // The miss list; the fused instance also needs the host rows now (for the
-  // rows loaded ahead), the plan-only instance writes them after the victims
-  // are ranked, so the loads never hold a barrier.
-  const int mpos0 = mpos;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (missbits & (1u << j)) {
-      if (COPY) m_h[mpos] = hm[j];
-      m_entry[mpos++] = i0 + j;
-    }
-
-  // Fused copy, first rows: each wavefront loads its first kCopyRowsInFlight
-  // rows of the first layer now, so the host link already works while the
-  // victims are ranked; they are stored once their slots are known.
-  constexpr int RIF = kCopyRowsInFlight;
-  u32x4 pre[RIF];
-  const bool have_pre = COPY && m_total > 0 && p.units <= kWave;
-  if (have_pre) {
-    lds_barrier();  // the miss list of every wavefront
-#pragma unroll
-    for (int q = 0; q < RIF; ++q) {
-      pre[q] = u32x4{0u, 0u, 0u, 0u};
-      const int j = wid + q * kResolveWaves;
-      if (j < m_total) {
-        const int64_t h = __builtin_amdgcn_readfirstlane(m_h[j]);
-        const bool ok = h >= 0 && h < p.host_rows[0];
-        const gu4* src = ok ? (const gu4*)p.host_pool[0] + h * p.units : (const gu4*)p.zero_row;
-        if (lane < p.units) pre[q] = src[lane];
-      }
-    }
-  }
-
-  // Step 4: victims, in (occupied, stamp, slot) order among non-hit slots.
   uint64_t key[SPT];
   unsigned cand = 0;
+  uint64_t kmine = ~0ull;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     key[j] = ((uint64_t)(sr[j] >= 0 ? 1u : 0u) << 32) | (uint64_t)((uint32_t)lr[j] ^ 0x80000000u);
-    if (s0 + j < S && !(hitm & (1u << j))) cand |= 1u << j;
+    if (s0 + j < S && !(hitm & (1u << j))) {
+      cand |= 1u << j;
+      kmine = key[j] < kmine ? key[j] : kmine;
+    }
   }
+  int mpre;  // misses in lower lanes of this wavefront
+  {
+    const int a0 = wave_sum_small<bits_for(KPT)>(n_hit);
+    const int a1 = wave_sum_small<bits_for(KPT)>(n_res);
+    const int a2 = wave_sum_small<bits_for(KPT)>(n_trip);
+    int wt = 0;
+    mpre = 0;
+#pragma unroll
+    for (int q = 0; q < bits_for(KPT); ++q) {
+      const uint64_t m = __ballot((my_miss >> q) & 1);
+      mpre += lane_prefix(m) << q;
+      wt += __popcll(m) << q;
+    }
+    const uint64_t km = wave_min_key(kmine);
+    if (lane == 0) {
+      scr[kScrStats + wid] = a0;
+      scr[kScrStats + 16 + wid] = a1;
+      scr[kScrStats + 32 + wid] = a2;
+      scr[kScrMiss + wid] = wt;
+      ((uint64_t*)(scr + kScrMin))[wid] = km;
+    }
+  }
+  // Ranking bitmaps [word][key] with a padded (odd) key stride, so that the
+  // lanes of one word, whose slots carry different keys, reach different
+  // LDS banks: bit s % 64 of word s / 64 of key d = slot s has key base + d.
+  const int NBIN = L.bins, W = L.words, BST = L.bins + 1;
+  uint64_t* bm = (uint64_t*)(smem + L.off_bits);    // [W][BST] slots of each key in the window
+  uint32_t* wpre = (uint32_t*)(smem + L.off_wpre);  // [W][BST] set bits of the key in earlier words
+  for (int x = tid; x < W * BST; x += kResolveThreads) bm[x] = 0ull;
+  lds_barrier();
+
+  // Step 4: the ordered miss list (ascending top-k index), and the misses'
+  // count m; then victims, in (occupied, stamp, slot) order among the
+  // candidates.  A window takes the keys base .. base + NBIN - 1 above the
+  // smallest remaining key: each key's candidates set their bits in that
+  // key's slot bitmap, each bitmap's words get exclusive popcount prefixes,
+  // and a candidate's rank is (victims so far) + (candidates of smaller keys
+  // in the window) + (candidates of its key at lower slots): the exact
+  // position in key-then-slot order, with three barriers per window.
+  // Keys spread over more than kMaxRankWindows windows fall back to a
+  // bitonic sort of the remaining candidates.
+  int m_total, mpos;
+  {
+    const uint32_t inc = wave_inclusive_sum(lane < kResolveWaves ? (uint32_t)scr[kScrMiss + lane] : 0u);
+    m_total = __builtin_amdgcn_readlane((int)inc, 63);
+    mpos = (wid > 0 ? __builtin_amdgcn_readlane((int)inc, wid - 1) : 0) + mpre;
+  }
+  const int mpos0 = mpos;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (missbits & (1u << j)) m_entry[mpos++] = i0 + j;
+
   int vr[SPT];  // rank of this slot among the victims, or -1
 #pragma unroll
   for (int j = 0; j < SPT; ++j) vr[j] = -1;
   int need = m_total, vbase = 0;
+  constexpr int RIF = kCopyRowsInFlight;
+  u32x4 pre[RIF];
+  bool have_pre = false;
+  const int wrd = s0 >> 6, bit0 = s0 & 63;  // this thread's slots share one bitmap word
+  if (NBIN > 0 && need > 0) {
 #pragma unroll 1
-  for (int round = 0; round < kVictimRounds && need > 0; ++round) {
-    uint64_t my = ~0ull;
+    for (int win = 0;; ++win) {
+      const uint64_t* kmin_part = (const uint64_t*)(scr + kScrMin) + 16 * (win & 1);
+      // the other half holds the next window's minima only after two more
+      // barriers; until then it takes this window's per-wave counts below
+      int* key0_part = scr + kScrMin + 32 * ((win + 1) & 1);
+      const uint64_t base = wave_min_key(lane < kResolveWaves ? kmin_part[lane] : ~0ull);
+      unsigned inwin = 0, at0 = 0;
+      int dd[SPT];
 #pragma unroll
-    for (int j = 0; j < SPT; ++j)
-      if ((cand & (1u << j)) && key[j] < my) my = key[j];
-    const uint64_t kmin =
-        block_min_key(my, (uint64_t*)(scr + kScrRoundMin + 32 * round));
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) cnt += ((cand & (1u << j)) && key[j] == kmin) ? 1 : 0;
-    int tot;
-    int pos = block_exscan_small<bits_for(SPT)>(cnt, scr + kScrRoundScan + 16 * round, &tot);
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      if ((cand & (1u << j)) && key[j] == kmin) {
-        if (pos < need) {
-          vr[j] = vbase + pos;
-          cand &= ~(1u << j);
+      for (int j = 0; j < SPT; ++j) {
+        const uint64_t d = key[j] - base;
+        dd[j] = (int)d;
+        if ((cand & (1u << j)) && d < (uint64_t)NBIN) {
+          inwin |= 1u << j;
+          at0 |= (d == 0 ? 1u : 0u) << j;
+          atomicOr((unsigned long long*)&bm[wrd * BST + dd[j]], 1ull << (bit0 + j));
         }
-        ++pos;
       }
+      // Candidates of the smallest key, counted per wavefront on the way: if
+      // they cover every remaining miss, their slot-order prefix is the rank
+      // and the window needs no word prefixes (a few misses, as on steps
+      // with high reuse).
+      int pre0;
+      {
+        const int c0 = __popc(at0);
+        int wt = 0;
+        pre0 = 0;
+#pragma unroll
+        for (int q = 0; q < bits_for(SPT); ++q) {
+          const uint64_t m = __ballot((c0 >> q) & 1);
+          pre0 += lane_prefix(m) << q;
+          wt += __popcll(m) << q;
+        }
+        if (lane == 0) key0_part[wid] = wt;
+      }
+      lds_barrier();
+      {
+        const uint32_t k0 = lane < kResolveWaves ? (uint32_t)key0_part[lane] : 0u;
+        const uint32_t inc0 = wave_inclusive_sum(k0);
+        const int tot0 = __builtin_amdgcn_readlane((int)inc0, 63);
+        if (tot0 >= need) {  // workgroup-uniform
+          int rk = (wid > 0 ? __builtin_amdgcn_readlane((int)inc0, wid - 1) : 0) + pre0;
+#pragma unroll
+          for (int j = 0; j < SPT; ++j)
+            if (at0 & (1u << j)) {
+              if (rk < need) vr[j] = vbase + rk;
+              ++rk;
+            }
+          if (COPY && win == 0) {
+            int mp = mpos0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+              if (missbits & (1u << j)) m_h[mp++] = host_row32(hraw[j]);
+          }
+          vbase += need;
+          need = 0;
+          break;
+        }
+      }
+      // Word prefixes of each key's bitmap (wavefront wid takes keys wid,
+      // wid + 16) and the number of candidates of each key.
+      if (COPY && win == 0) {
+        int mp = mpos0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (missbits & (1u << j)) m_h[mp++] = host_row32(hraw[j]);
+      }
+      for (int bin = wid; bin < NBIN; bin += kResolveWaves) {
+        uint32_t carry = 0;
+        for (int w0 = 0; w0 < W; w0 += kWave) {
+          const int w = w0 + lane;
+          const uint32_t pc = w < W ? (uint32_t)__popcll(bm[w * BST + bin]) : 0u;
+          const uint32_t inc = wave_inclusive_sum(pc);
+          if (w < W) wpre[w * BST + bin] = carry + inc - pc;
+          carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+        }
+        if (lane == 0) scr[kScrBtot + bin] = (int)carry;
+      }
+      lds_barrier();
+      // Fused copy, first rows: each wavefront loads its first
+      // kCopyRowsInFlight rows of the first layer now (their host rows are
+      // in the miss list), so the host link works while the ranks are
+      // computed; the rows are stored once their slots are known.
+      if (COPY && win == 0 && p.units <= kWave) {
+        have_pre = true;
+#pragma unroll
+        for (int q = 0; q < RIF; ++q) {
+          pre[q] = u32x4{0u, 0u, 0u, 0u};
+          const int j = wid + q * kResolveWaves;
+          if (j < m_total) {
+            const int64_t h = __builtin_amdgcn_readfirstlane(m_h[j]);
+            const bool ok = h >= 0 && h < p.host_rows[0];
+            const gu4* src = ok ? (const gu4*)p.host_pool[0] + h * p.units : (const gu4*)p.zero_row;
+            if (lane < p.units) pre[q] = src[lane];
+          }
+        }
+      }
+      const uint32_t bcnt = lane < NBIN ? (uint32_t)scr[kScrBtot + lane] : 0u;
+      const uint32_t binc = wave_inclusive_sum(bcnt);
+      const int tot = __builtin_amdgcn_readlane((int)binc, 63);
+      const int cexcl = (int)(binc - bcnt);  // lane d: candidates of keys below base + d
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        const int d = (inwin & (1u << j)) ? dd[j] : 0;
+        const int below = __shfl(cexcl, d, kWave);
+        if (inwin & (1u << j)) {
+          const uint64_t word = bm[wrd * BST + d];
+          const int rank = below + (int)wpre[wrd * BST + d] +
+                           __popcll(word & ((1ull << (bit0 + j)) - 1ull));
+          if (rank < need) vr[j] = vbase + rank;
+        }
+      }
+      cand &= ~inwin;
+      const int take = tot < need ? tot : need;
+      vbase += take;
+      need -= take;
+      if (need == 0 || win + 1 == kMaxRankWindows) break;
+      // Next window: the smallest key left, once every thread is done
+      // reading the bitmaps.
+      lds_barrier();
+      for (int x = tid; x < W * BST; x += kResolveThreads) bm[x] = 0ull;
+      uint64_t km = ~0ull;
+#pragma unroll
+      for (int j = 0; j < SPT; ++j)
+        if ((cand & (1u << j)) && key[j] < km) km = key[j];
+      km = wave_min_key(km);
+      if (lane == 0) ((uint64_t*)(scr + kScrMin))[16 * ((win + 1) & 1) + wid] = km;
+      lds_barrier();
     }
-    const int take = tot < need ? tot : need;
-    vbase += take;
-    need -= take;
   }
-  if (need > 0) {  // many distinct stamps among the victims: sort the rest
+  if (need > 0) {  // keys spread over many windows: sort the remaining candidates
     const int N = L.sort_size;
-    lds_barrier();  // the table region is reused for the sort
+    lds_barrier();  // the table and bitmap regions are reused for the sort
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int s = s0 + j;
@@ -546,24 +701,23 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         const int v = vrank[s0 + j];
         if (v >= 0) vr[j] = v;
       }
-  }
-  if (!COPY) {
-    int mp = mpos0;
+    if (COPY && NBIN == 0) {  // the miss list's host rows, not yet written
+      int mp = mpos0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (missbits & (1u << j)) m_h[mp++] = hm[j];
+      for (int j = 0; j < KPT; ++j)
+        if (missbits & (1u << j)) m_h[mp++] = host_row32(hraw[j]);
+    }
+    lds_barrier();  // the victim list is rewritten below
   }
-  lds_barrier();
 
-  // Step 5: the victim of rank j takes the j-th miss: its owner sets token
-  // and row ID and writes one entry of the compact plan.  The fused copy keeps
-  // its own copy of the plan in the (now dead) table region.  Then every
+  // Step 5: the victim of rank j takes the j-th miss: its owner sets token,
+  // row ID and the device row of plan entry j; the miss's owner writes the
+  // host row of plan entry j.  The fused copy keeps the plan's device rows
+  // in the victim list (its host rows are the miss list's).  Then every
   // thread writes its slot run back once: stamps of hit and victim slots,
   // tokens of victim slots (vector stores, not one scattered store per slot).
   int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
   int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
-  int64_t* f_src = (int64_t*)(smem + L.off_hash);          // [k]
-  int32_t* f_dst = (int32_t*)(smem + L.off_hash + 8 * (size_t)k);  // [k]
   unsigned vict = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
@@ -574,14 +728,16 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     sr[j] = e_tok[i];
     const int row = rowbase + s0 + j;
     outb[i] = row;
-    const int64_t h = m_h[v];  // -1 for a row outside [0, 2^31)
-    psrc[v] = h;
     pdst[v] = row;
-    if (COPY) {
-      f_src[v] = h;
-      f_dst[v] = row;
-    }
+    if (COPY) victim[v] = row;
   }
+  {
+    int mp = mpos0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (missbits & (1u << j)) psrc[mp++] = hraw[j];
+  }
+  const int32_t c = (int32_t)((uint32_t)clk_now + 1u);
   const unsigned touched = hitm | vict;
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
@@ -617,17 +773,20 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       const bool first = u == wu;
       const gu4* src[RIF];
       gu4* dst[RIF];
+      bool dok[RIF];
 #pragma unroll
       for (int q = 0; q < RIF; ++q) {
         const bool real = u + q * kResolveWaves < total;
         const int uq = real ? u + q * kResolveWaves : u;
         const int l = uq / m_total, j = uq - l * m_total;
-        const int64_t h = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)f_src[j]) |
-                          ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(f_src[j] >> 32)) << 32);
-        const int d = __builtin_amdgcn_readfirstlane(f_dst[j]);
+        const int64_t h = __builtin_amdgcn_readfirstlane(m_h[j]);   // -1: outside [0, 2^31)
+        const int d = __builtin_amdgcn_readfirstlane(victim[j]);    // the plan's device row
         const bool ok = h >= 0 && h < p.host_rows[l];
+        // every miss's row is one of this request's hot rows; the check keeps
+        // a store inside them whatever the list holds
+        dok[q] = d >= rowbase && d < rowbase + S;
         src[q] = ok ? (const gu4*)p.host_pool[l] + h * U : (const gu4*)p.zero_row;
-        dst[q] = (gu4*)p.dev_pool[l] + (int64_t)d * U;
+        dst[q] = (gu4*)p.dev_pool[l] + (int64_t)(dok[q] ? d : rowbase) * U;
         copy_trips += (real && !ok) ? 1 : 0;
       }
       for (int part = lane; part < U; part += kWave) {
@@ -639,7 +798,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
           else v[q] = src[q][part];
         }
 #pragma unroll
-        for (int q = 0; q < RIF; ++q) dst[q][part] = v[q];
+        for (int q = 0; q < RIF; ++q)
+          if (dok[q]) dst[q][part] = v[q];
       }
     }
   }

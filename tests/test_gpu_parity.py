@@ -142,7 +142,48 @@ def test_corrupt_state_and_tripwires(mode, layers):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("S,k", [(4096, 4096), (8192, 4096), (16384, 1976)])
+@pytest.mark.parametrize("spread", [1, 20, 80, 130, 200, 400])
+def test_victim_keys_spread_over_windows(mode, spread):
+    """Victims are ranked by windows of up to 32 consecutive keys above the
+    smallest remaining one.  Here every request starts with about 3% empty
+    slots whose stamps are 0, 1 or 2 (their own window, first) and occupied
+    slots whose stamps take `spread` consecutive values, so the first step's
+    ~235 victims per request need two windows (spread 1, 20), three (80),
+    three or four (130), four or five (200) or seven or eight (400); beyond
+    the four windows allowed the bitonic-sort fallback finishes the ranking.
+    Each step must match the oracle bit for bit."""
+    print("[spread %s] %d" % (mode, spread), flush=True)
+    S, k = 512, 256
+    n0 = [5000 + 331 * b for b in range(9)]
+    w = synth("spread", 61 + spread, R=10, S=S, k=k, steps=3, n0=n0, keep=64)
+    pair = Pair(w, make_host_pools(w), mode=mode)
+    try:
+        rng = np.random.default_rng(spread)
+        st = np.empty((w.R, S), np.int32)
+        lru = np.empty((w.R, S), np.int32)
+        for r in range(w.R):
+            st[r] = rng.choice(4000, size=S, replace=False)   # distinct valid tokens
+            lru[r] = 1000 + rng.integers(0, spread, size=S)
+            empty = rng.random(S) < 0.03
+            st[r, empty] = -1
+            lru[r, empty] = rng.integers(0, 3, size=int(empty.sum()))
+        clk = np.full(w.R, 1000 + spread + 5, np.int32)
+        for t, a in ((pair.st, st), (pair.lru, lru), (pair.clk, clk)):
+            t.copy_(torch.from_numpy(a))
+        pair.ost.slot_tokens[:], pair.ost.lru_slots[:], pair.ost.lru_clock[:] = st, lru, clk
+        for step in range(w.steps):
+            dst, src = pair.gpu_step(step)
+            o = pair.oracle_step(step, dst, src)
+            torch.cuda.synchronize()
+            pair.compare_step(step, o)
+        pair.compare_pools()
+        assert pair.ost.stats[1] > 0
+    finally:
+        pair.close()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("S,k", [(4096, 4096), (8192, 4096), (16384, 2004)])
 def test_lds_budget_corners(mode, S, k):
     """The largest slot / top-k pairs the LDS budget allows: the table with
     two cells per entry, 4 and 8 top-k entries and 4, 8 and 16 slots per

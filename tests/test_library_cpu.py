@@ -195,7 +195,7 @@ def test_init_rejects_a_device_pool_too_small_for_the_hot_rows():
 
 
 @pytest.mark.parametrize("S,k,fits", [(4096, 2048, True), (4096, 4096, True), (8192, 4096, True),
-                                      (16384, 1976, True), (16384, 1984, False),
+                                      (16384, 2004, True), (16384, 2008, False),
                                       (16384, 4096, False)])
 def test_lds_budget_limits_stated_in_the_header(S, k, fits):
     """The header's limits on max_top_k per slot count: shapes within them
