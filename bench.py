@@ -156,12 +156,12 @@ def time_calls(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def mixed_residency_legs(hs, torch, stream, reuses=(0.5, 0.99, 1.0)):
+def mixed_residency_legs(hs, torch, stream, reuses=(0.5, 0.9, 0.99, 1.0)):
     """Mixed residency: 128 requests of 131072 tokens whose last 16384 tokens
     sit in resident pages of 64 (resolved in place), 4096 hot slots,
     top-2048, 32 steps from cold per reuse fraction.  50 % reuse is the
-    miss-heavy case, 99 % the hit-heavy one, 100 % a diagnostic with no miss
-    after step 0.  Per fraction: step 0 (cold) timed alone; steps 1..31 timed
+    miss-heavy case, 90 % the middle of the sweep, 99 % the hit-heavy one,
+    100 % a diagnostic with no miss after step 0.  Per fraction: step 0 (cold) timed alone; steps 1..31 timed
     through hisparse_resolve (one launch per step at this batch); then the
     same steps replayed from the state after step 0 through the plan-only
     entry point, back to back, for the hit path against HBM."""
