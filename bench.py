@@ -406,6 +406,117 @@ def next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, warmup, ste
     return res
 
 
+PHASE_NAMES = (
+    "entry to first barrier: request loads issued, LDS table cleared",
+    "step 1: validity, resident pages, table inserts",
+    "step 2: every slot probes the table, hit slots",
+    "step 3: hits, misses, host-row loads issued, per-wave partials",
+    "step 4: victim ranking (windows or sort)",
+    "step 5: plan, row IDs and slot state written",
+    "to the end (fused: the miss copy)",
+)
+
+
+def phase_summary(tr, rows):
+    """Per-phase durations of the plan kernel from its trace ([rows][waves]
+    [points][clock, real-time]) over the given batch rows: a phase ends when
+    the last wavefront of the row reaches its point (the barrier after it
+    waits for every wavefront); the first starts when the first wavefront
+    enters.  Returns (cycles per phase, real-time ticks per phase) summed
+    over the rows, and the rows' windows / sort-fallback info."""
+    cyc = tr[rows, :, :8, 0].astype(np.int64)
+    rt = tr[rows, :, :8, 1].astype(np.int64)
+    assert (cyc > 0).all() and (rt > 0).all(), "a traced row missed a phase point"
+    c_end = cyc.max(axis=1)
+    r_end = rt.max(axis=1)
+    c_end[:, 0] = cyc[:, :, 0].min(axis=1)
+    r_end[:, 0] = rt[:, :, 0].min(axis=1)
+    return (np.diff(c_end, axis=1).sum(axis=0), np.diff(r_end, axis=1).sum(axis=0),
+            tr[rows, 0, 8, 0].astype(np.int64), tr[rows, 0, 8, 1].astype(np.int64),
+            rt[:, :, 0].min(axis=1), rt[:, :, 7].max(axis=1))
+
+
+def plan_phases(w, g, hs, torch, stream, args):
+    """The plan kernel's phase trace over the timed steps (plan-only and
+    fused instances, from the same state), and the floor kernels of its
+    launch shape, all timed with HIP events on the launch stream."""
+    def plan(i, fused=False):
+        fn = hs.hisparse_resolve if fused else hs.hisparse_resolve_plan
+        fn(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i], g["seq"][i], g["locs"], None,
+           g["st"], g["lru"], g["clk"], g["out"], None)
+
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        plan(i)
+        hs.hisparse_gather_copy(g["pool"], stream, w.B, 0, w.L, None)
+    torch.cuda.synchronize()
+    snap = (g["st"].clone(), g["lru"].clone(), g["clk"].clone())
+
+    def restore():
+        g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+        torch.cuda.synchronize()
+
+    res = {}
+    for fused in (False, True):
+        restore()
+        cyc = rt = 0
+        wins, sorts, spans = [], [], []
+        n_rows = 0
+        for j in range(args.steps):
+            i = args.warmup + j
+            hs.hisparse_diag_phase_clear()
+            plan(i, fused)
+            torch.cuda.synchronize()
+            tr = hs.hisparse_diag_phase_read()
+            rows = np.nonzero(w.seq_lens[i] > w.S)[0]
+            rows = rows[rows < tr.shape[0]]
+            c, r, wi, so, t0, t1 = phase_summary(tr, rows)
+            cyc = cyc + c
+            rt = rt + r
+            wins += wi.tolist()
+            sorts += so.tolist()
+            spans.append(float(t1.max() - t0.min()) / 100.0)   # real-time ticks: 100 MHz
+            n_rows += len(rows)
+        ghz = float(cyc.sum()) / float(rt.sum()) / 10.0
+        res["fused" if fused else "plan_only"] = {
+            "rows_per_step": n_rows // args.steps,
+            "phases": [{"phase": PHASE_NAMES[q], "cycles": round(float(cyc[q]) / n_rows),
+                        "us": round(float(rt[q]) / n_rows / 100.0, 3)} for q in range(7)],
+            "row_total_us": round(float(rt.sum()) / n_rows / 100.0, 3),
+            "clock_ghz": round(ghz, 3),
+            "grid_span_us": round(float(np.mean(spans)), 3),
+            "windows_per_row": {str(v): wins.count(v) for v in sorted(set(wins))},
+            "sort_fallback_rows": int(sum(sorts)),
+        }
+    # events: the plan-only launches back to back, as in the main benchmark
+    restore()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for j in range(args.steps):
+        plan(args.warmup + j)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["plan_only_us_events"] = round(e0.elapsed_time(e1) / args.steps * 1e3, 3)
+    # floors of the same launch shape on the same inputs
+    scratch = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    i_last = args.warmup + args.steps - 1
+    floors = {}
+    for kind, name in enumerate(("empty", "one_round_trip", "two_round_trips", "memory_chain")):
+        fn = lambda n, kind=kind: hs.hisparse_diag_floor(
+            stream, kind, w.B, w.k, w.S, w.R, w.max_seq_len, g["req"], g["topk"][i_last],
+            g["st"], g["lru"], g["locs"], scratch, launches=n)
+        fn(10)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn(200)        # the launch loop runs in the library: events time the kernels
+        e1.record(stream)
+        torch.cuda.synchronize()
+        floors[name] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
+    res["floors_us"] = floors
+    return res
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -471,7 +582,12 @@ def main():
                          "(fused) and 5 decode calls (for rocprofv3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 plain device copies of 256 MiB (counter calibration)")
+    ap.add_argument("--plan-phases", action="store_true",
+                    help="only the plan kernel's phase trace (diagnostic library) over the "
+                         "timed steps and the floor kernels of its launch shape")
     args = ap.parse_args()
+    if args.plan_phases:
+        os.environ["HISPARSE_LIBRARY"] = "diag"   # read when the package is imported
     if args.gpus != 1:
         print("bench.py measures one GPU only: the resolver shards by request with no "
               "exchange, so a multi-GPU figure is N independent copies of this one; "
@@ -504,6 +620,15 @@ def main():
     fill_host_rows_mla(host_buf.torch((w.host_pool_rows, ROW_BYTES)), seed=200, gen_device="cuda")
     g = setup_gpu(w, torch, hs, host_buf)
     stream = torch.cuda.current_stream()
+    if args.plan_phases:
+        assert hs.is_diag_library()
+        res = plan_phases(w, g, hs, torch, stream, args)
+        res.update({"metric": "plan kernel phases and floors", "n_gpus": 1, "steps": args.steps,
+                    "warmup": args.warmup,
+                    "config": {"workload": "dsa_decode: 64 rows of 32768-131072 tokens + 8 "
+                               "fast-path rows, top-2048, 4096 slots"}})
+        print(json.dumps(res), flush=True)
+        return
 
     def step(i):
         """One decode step: the single-call entry point.  At this batch it runs

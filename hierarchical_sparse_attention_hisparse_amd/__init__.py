@@ -6,7 +6,10 @@ kernels of that library; this package only marshals arguments (torch tensors
 for device memory, torch streams) and checks shapes and dtypes so that a
 wrong tensor is rejected on the host instead of being read out of bounds on
 the GPU.  There is no fallback: if the library is missing, importing the
-binding raises.
+binding raises.  With HISPARSE_LIBRARY=diag set before the import, the
+binding loads ``libhisparse_diag.so`` instead: the same entry points with the
+plan kernel's phase trace compiled in, plus the diagnostic ones of
+``include/hisparse_diag.h`` (phase trace, floor kernels).
 """
 from ._binding import (  # noqa: F401
     HisparseError,
@@ -15,6 +18,9 @@ from ._binding import (  # noqa: F401
     STAT_NAMES,
     hisparse_decode_layers_overlapped,
     hisparse_destroy_pool,
+    hisparse_diag_floor,
+    hisparse_diag_phase_clear,
+    hisparse_diag_phase_read,
     hisparse_gather_copy,
     hisparse_gather_copy_step,
     hisparse_host_alloc,
@@ -29,6 +35,7 @@ from ._binding import (  # noqa: F401
     hisparse_resolve_steps,
     hisparse_sparse_mla_decode,
     hisparse_sparse_mla_decode_noalloc,
+    is_diag_library,
     library_path,
     load_library,
 )

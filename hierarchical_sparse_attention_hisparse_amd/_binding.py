@@ -10,7 +10,10 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libhisparse.so")
+# HISPARSE_LIBRARY=diag loads the diagnostic build (the same entry points, the
+# plan kernel's phase trace compiled in, and the floor kernels).
+_DIAG = os.environ.get("HISPARSE_LIBRARY", "") == "diag"
+_LIB_PATH = os.path.join(_HERE, "libhisparse_diag.so" if _DIAG else "libhisparse.so")
 _lib = None
 
 STAT_NAMES = ("hot_hits", "misses", "resident_hits", "fast_path", "tripwires")
@@ -63,7 +66,7 @@ def load_library():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
-        raise ImportError("libhisparse.so is not built: run `python -m "
+        raise ImportError(os.path.basename(_LIB_PATH) + " is not built: run `python -m "
                           "hierarchical_sparse_attention_hisparse_amd.build` "
                           "(or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
@@ -104,8 +107,19 @@ def load_library():
     lib.hisparse_sparse_mla_decode_noalloc.restype = I
     lib.hisparse_sparse_mla_decode_noalloc.argtypes = [V, I32, I32, I32, V, I64, I32, V, V,
                                                        ctypes.c_float, V]
+    if _DIAG:
+        lib.hisparse_diag_phase_clear.restype = I
+        lib.hisparse_diag_phase_clear.argtypes = []
+        lib.hisparse_diag_phase_read.restype = I
+        lib.hisparse_diag_phase_read.argtypes = [V, ctypes.c_size_t]
+        lib.hisparse_diag_floor.restype = I
+        lib.hisparse_diag_floor.argtypes = [V, I32, I32, I32, I32, I32, I64, V, V, V, V, V, V, I32]
     _lib = lib
     return lib
+
+
+def is_diag_library() -> bool:
+    return _DIAG
 
 
 def hisparse_last_error() -> str:
@@ -419,3 +433,45 @@ def hisparse_decode_layers_overlapped(pool, stream, batch, heads, top_k, q_per_l
         pool.handle, _stream_handle(stream), batch, heads, top_k, ctypes.cast(qs, ctypes.c_void_p), lp, ctypes.c_float(softmax_scale),
         ctypes.cast(outs, ctypes.c_void_p), sp), "hisparse_decode_layers_overlapped")
 
+
+
+# ------------------------------------------------- diagnostic library only --
+TRACE_ROWS, TRACE_WAVES, TRACE_POINTS = 256, 16, 9   # include/hisparse_diag.h
+
+
+def _diag_library():
+    if not _DIAG:
+        raise RuntimeError("the diagnostic entry points need HISPARSE_LIBRARY=diag "
+                           "(libhisparse_diag.so) set before the package is imported")
+    return load_library()
+
+
+def hisparse_diag_phase_clear():
+    _check_rc(_diag_library().hisparse_diag_phase_clear(), "hisparse_diag_phase_clear")
+
+
+def hisparse_diag_phase_read() -> np.ndarray:
+    """The plan kernel's phase trace as uint64 [rows, waves, points, 2]."""
+    out = np.zeros((TRACE_ROWS, TRACE_WAVES, TRACE_POINTS, 2), dtype=np.uint64)
+    _check_rc(_diag_library().hisparse_diag_phase_read(out.ctypes.data, out.size),
+              "hisparse_diag_phase_read")
+    return out
+
+
+def hisparse_diag_floor(stream, kind, batch, top_k=1, slots=1, max_requests=1, max_seq_len=1,
+                        req_idx=None, top_k_tokens=None, slot_tokens=None, lru_slots=None,
+                        host_cache_locs=None, out=None, launches=1):
+    """``launches`` back-to-back launches of a floor kernel of the plan's
+    shape (kind 0-3, see include/hisparse_diag.h) on ``stream``; tensors as
+    hisparse_resolve takes them, ``out`` int32 [batch, top_k] scratch."""
+    import torch
+    req = _dev(req_idx, torch.int32, (batch,), "req_idx", allow_none=kind == 0)
+    tk = _dev(top_k_tokens, torch.int32, (batch, top_k), "top_k_tokens", allow_none=kind != 3)
+    st = _dev(slot_tokens, torch.int32, (max_requests, slots), "slot_tokens", allow_none=kind < 2)
+    lru = _dev(lru_slots, torch.int32, (max_requests, slots), "lru_slots", allow_none=kind < 2)
+    locs = _dev(host_cache_locs, torch.int64, (max_requests, max_seq_len), "host_cache_locs",
+                allow_none=kind != 3)
+    op = _dev(out, torch.int32, (batch, top_k), "out", allow_none=kind == 0)
+    _check_rc(_diag_library().hisparse_diag_floor(
+        _stream_handle(stream), kind, batch, top_k, slots, max_requests, max_seq_len,
+        req, tk, st, lru, locs, op, launches), "hisparse_diag_floor")

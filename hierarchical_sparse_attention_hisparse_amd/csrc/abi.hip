@@ -241,6 +241,14 @@ int noalloc_scratch(void** out) {
 
 }  // namespace
 
+int hisparse::report_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 extern "C" {
 
 const char* hisparse_last_error(void) { return g_err; }

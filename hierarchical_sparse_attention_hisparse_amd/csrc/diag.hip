@@ -1,0 +1,165 @@
+// diag.hip -- entry points of the diagnostic library (libhisparse_diag.so):
+// the plan kernel's phase trace, read out, and floor kernels of the plan
+// kernel's launch shape (one 1024-thread workgroup per batch row), which
+// price the launch, its dependent global round trips and its memory chain
+// without the computation between them.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/hisparse.h"
+#include "../../include/hisparse_diag.h"
+#include "common.h"
+#include "kernels.h"
+
+static_assert(HISPARSE_TRACE_ROWS == hisparse::kTraceRows, "trace rows");
+static_assert(HISPARSE_TRACE_WAVES == hisparse::kResolveWaves, "trace waves");
+static_assert(HISPARSE_TRACE_POINTS == hisparse::kTracePoints, "trace points");
+
+namespace hisparse {
+namespace {
+
+constexpr int kFloorThreads = kResolveThreads;
+constexpr int kFloorMaxK = 4096;  // entries per row: at most 4 per thread
+
+struct FloorParams {
+  int32_t k, S, R;
+  int64_t max_seq_len;
+  const int32_t* req;
+  const int32_t* topk;
+  const int32_t* st;
+  const int32_t* lru;
+  const int64_t* locs;
+  int32_t* out;
+};
+
+__device__ inline int clamp_req(int r, int R) { return r < 0 ? 0 : (r >= R ? R - 1 : r); }
+
+__global__ __launch_bounds__(kFloorThreads) void floor_empty_kernel() {}
+
+// One round trip: the request row, stored to the row's outputs.
+__global__ __launch_bounds__(kFloorThreads) void floor_one_kernel(FloorParams p) {
+  const int b = blockIdx.x;
+  const int r = p.req[b];
+  for (int i = threadIdx.x; i < p.k; i += kFloorThreads) p.out[(int64_t)b * p.k + i] = r;
+}
+
+// Two dependent round trips: the request row, then its slot map and stamps
+// (coalesced), folded per thread and stored.
+__global__ __launch_bounds__(kFloorThreads) void floor_two_kernel(FloorParams p) {
+  const int b = blockIdx.x;
+  const int r = clamp_req(p.req[b], p.R);
+  const int32_t* st = p.st + (int64_t)r * p.S;
+  const int32_t* lru = p.lru + (int64_t)r * p.S;
+  int acc = 0;
+  for (int s = threadIdx.x; s < p.S; s += kFloorThreads) acc += st[s] ^ lru[s];
+  for (int i = threadIdx.x; i < p.k; i += kFloorThreads) p.out[(int64_t)b * p.k + i] = acc;
+}
+
+// The plan's memory chain: top-k row and request row; slot map and stamps;
+// a workgroup exchange; one host location per entry, whose address depends
+// on the exchanged slot data (as a miss's does); row IDs stored.
+__global__ __launch_bounds__(kFloorThreads) void floor_chain_kernel(FloorParams p) {
+  __shared__ int part[kFloorThreads / kWave];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  int t[kFloorMaxK / kFloorThreads];
+#pragma unroll
+  for (int j = 0; j < kFloorMaxK / kFloorThreads; ++j) {
+    const int i = tid + j * kFloorThreads;
+    t[j] = i < p.k ? p.topk[(int64_t)b * p.k + i] : 0;
+  }
+  const int r = clamp_req(p.req[b], p.R);
+  const int32_t* st = p.st + (int64_t)r * p.S;
+  const int32_t* lru = p.lru + (int64_t)r * p.S;
+  int acc = 0;
+  for (int s = tid; s < p.S; s += kFloorThreads) acc += st[s] ^ lru[s];
+  for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  if (lane == 0) part[wid] = acc;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < kFloorThreads / kWave; ++w) tot += part[w];
+  const int64_t* locr = p.locs + (int64_t)r * p.max_seq_len;
+#pragma unroll
+  for (int j = 0; j < kFloorMaxK / kFloorThreads; ++j) {
+    const int i = tid + j * kFloorThreads;
+    if (i < p.k) {
+      int64_t pos = t[j] < 0 ? 0 : (t[j] >= p.max_seq_len ? p.max_seq_len - 1 : t[j]);
+      pos = tot == INT_MIN ? 0 : pos;  // the address waits for the slot data
+      p.out[(int64_t)b * p.k + i] = (int32_t)locr[pos];
+    }
+  }
+}
+
+}  // namespace
+}  // namespace hisparse
+
+using namespace hisparse;
+
+extern "C" {
+
+int hisparse_diag_phase_clear(void) {
+  const hipError_t e = phase_trace_clear();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return report_error(HISPARSE_EHIP, "phase trace clear: %s", hipGetErrorString(e));
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_diag_phase_read(uint64_t* host_out, size_t count) {
+  if (!host_out) return report_error(HISPARSE_EINVAL, "host_out is NULL");
+  if (count != (size_t)HISPARSE_TRACE_WORDS)
+    return report_error(HISPARSE_EINVAL, "count %zu != %d", count, HISPARSE_TRACE_WORDS);
+  const hipError_t e = phase_trace_read(host_out, count);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return report_error(HISPARSE_EHIP, "phase trace read: %s", hipGetErrorString(e));
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k, int32_t slots,
+                        int32_t max_requests, int64_t max_seq_len, const int32_t* req_idx,
+                        const int32_t* top_k_tokens, const int32_t* slot_tokens,
+                        const int32_t* lru_slots, const int64_t* host_cache_locs, int32_t* out,
+                        int32_t launches) {
+  if (kind < 0 || kind > 3) return report_error(HISPARSE_EINVAL, "kind %d not in [0, 3]", kind);
+  if (launches < 1 || launches > (1 << 20))
+    return report_error(HISPARSE_EINVAL, "launches %d not in [1, 1048576]", launches);
+  if (batch < 1 || batch > 65535) return report_error(HISPARSE_EINVAL, "batch %d not in [1, 65535]", batch);
+  if (kind >= 1) {
+    if (!req_idx || !out) return report_error(HISPARSE_EINVAL, "req_idx or out is NULL");
+    if (top_k < 1 || top_k > kFloorMaxK)
+      return report_error(HISPARSE_EINVAL, "top_k %d not in [1, %d]", top_k, kFloorMaxK);
+    if (max_requests < 1) return report_error(HISPARSE_EINVAL, "max_requests %d < 1", max_requests);
+  }
+  if (kind >= 2) {
+    if (!slot_tokens || !lru_slots) return report_error(HISPARSE_EINVAL, "slot state is NULL");
+    if (slots < 1 || slots > kMaxSlots)
+      return report_error(HISPARSE_EINVAL, "slots %d not in [1, %d]", slots, kMaxSlots);
+  }
+  if (kind == 3) {
+    if (!top_k_tokens || !host_cache_locs)
+      return report_error(HISPARSE_EINVAL, "top_k_tokens or host_cache_locs is NULL");
+    if (max_seq_len < 1) return report_error(HISPARSE_EINVAL, "max_seq_len %lld < 1", (long long)max_seq_len);
+  }
+  FloorParams p{top_k, slots, max_requests, max_seq_len, req_idx, top_k_tokens,
+                slot_tokens, lru_slots, host_cache_locs, out};
+  const hipStream_t s = (hipStream_t)stream;
+  const dim3 g(batch), t(kFloorThreads);
+  for (int n = 0; n < launches; ++n) {
+    switch (kind) {
+      case 0: hipLaunchKernelGGL(floor_empty_kernel, g, t, 0, s); break;
+      case 1: hipLaunchKernelGGL(floor_one_kernel, g, t, 0, s, p); break;
+      case 2: hipLaunchKernelGGL(floor_two_kernel, g, t, 0, s, p); break;
+      default: hipLaunchKernelGGL(floor_chain_kernel, g, t, 0, s, p); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return report_error(HISPARSE_EHIP, "floor kernel launch: %s", hipGetErrorString(e));
+  }
+  return HISPARSE_OK;
+}
+
+}  // extern "C"

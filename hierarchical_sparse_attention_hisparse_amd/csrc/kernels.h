@@ -132,4 +132,15 @@ int decode_splits(int batch, int heads, int k);
 size_t decode_workspace_bytes(int batch, int heads, int splits);
 size_t decode_workspace_max_bytes(int max_batch, int max_heads);
 
+// Records the message of a failing call for hisparse_last_error (the error
+// channel every entry point shares) and returns `code`.
+int report_error(int code, const char* fmt, ...);
+
+#ifdef HISPARSE_PHASE_TRACE
+// The plan kernel's phase trace (diagnostic build): zeroed, or copied out as
+// [kTraceRows][kResolveWaves][kTracePoints][2] uint64; both wait for the device.
+hipError_t phase_trace_clear();
+hipError_t phase_trace_read(uint64_t* host, size_t count);
+#endif
+
 }  // namespace hisparse

@@ -36,6 +36,35 @@
 
 namespace hisparse {
 
+#ifdef HISPARSE_PHASE_TRACE
+// Phase trace (diagnostic build only): lane 0 of each wavefront of the batch
+// rows below kTraceRows stores the shader clock and the 100 MHz real-time
+// counter at each phase point; point 8 holds the ranking windows used and
+// whether the sort fallback ran.
+__device__ unsigned long long g_phase_trace[kTraceRows][kResolveWaves][kTracePoints][2];
+#define PHASE_POINT(q)                                                         \
+  do {                                                                         \
+    if (lane == 0 && b < kTraceRows) {                                         \
+      g_phase_trace[b][wid][q][0] = (unsigned long long)clock64();             \
+      g_phase_trace[b][wid][q][1] = (unsigned long long)wall_clock64();        \
+    }                                                                          \
+  } while (0)
+#define PHASE_INFO(nwin, sorted)                                               \
+  do {                                                                         \
+    if (lane == 0 && b < kTraceRows) {                                         \
+      g_phase_trace[b][wid][8][0] = (unsigned long long)(nwin);                \
+      g_phase_trace[b][wid][8][1] = (unsigned long long)(sorted);              \
+    }                                                                          \
+  } while (0)
+#else
+#define PHASE_POINT(q) \
+  do {                 \
+  } while (0)
+#define PHASE_INFO(nwin, sorted) \
+  do {                           \
+  } while (0)
+#endif
+
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -198,6 +227,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wid = tid / kWave;
+  PHASE_POINT(0);
   const int k = p.k, S = p.S;
   int32_t* outb = p.out + (int64_t)b * k;
   const int32_t* tk = p.topk + (int64_t)b * k;
@@ -327,6 +357,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (i0 + j < k) e_hit[i0 + j] = INT_MAX;
+  PHASE_POINT(1);
   // Barriers below order LDS only: no thread reads global memory that another
   // thread of the workgroup wrote, so the slot-state loads stay in flight
   // through step 1 and the row-ID and stamp stores never hold a barrier.
@@ -366,6 +397,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       h = (h + 1) & (HS - 1);
     }
   }
+  PHASE_POINT(2);
   lds_barrier();
 
   // Step 2: probe the table with every slot's token; the SPT probes of a
@@ -417,6 +449,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     for (int j = 0; j < SPT; ++j)
       if (hidx[j] >= 0) atomicMin(&e_hit[hidx[j]], s0 + j);
   }
+  PHASE_POINT(3);
   lds_barrier();
 
   // Step 3: hits and misses.  An entry's hit slot is the one its e_hit
@@ -494,6 +527,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   uint64_t* bm = (uint64_t*)(smem + L.off_bits);    // [W][BST] slots of each key in the window
   uint32_t* wpre = (uint32_t*)(smem + L.off_wpre);  // [W][BST] set bits of the key in earlier words
   for (int x = tid; x < W * BST; x += kResolveThreads) bm[x] = 0ull;
+  PHASE_POINT(4);
   lds_barrier();
 
   // Step 4: the ordered miss list (ascending top-k index), and the misses'
@@ -525,9 +559,15 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   u32x4 pre[RIF];
   bool have_pre = false;
   const int wrd = s0 >> 6, bit0 = s0 & 63;  // this thread's slots share one bitmap word
+#ifdef HISPARSE_PHASE_TRACE
+  int trace_windows = 0;
+#endif
   if (NBIN > 0 && need > 0) {
 #pragma unroll 1
     for (int win = 0;; ++win) {
+#ifdef HISPARSE_PHASE_TRACE
+      trace_windows = win + 1;
+#endif
       const uint64_t* kmin_part = (const uint64_t*)(scr + kScrMin) + 16 * (win & 1);
       // the other half holds the next window's minima only after two more
       // barriers; until then it takes this window's per-wave counts below
@@ -657,6 +697,9 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       lds_barrier();
     }
   }
+#ifdef HISPARSE_PHASE_TRACE
+  PHASE_INFO(trace_windows, need > 0 ? 1 : 0);
+#endif
   if (need > 0) {  // keys spread over many windows: sort the remaining candidates
     const int N = L.sort_size;
     lds_barrier();  // the table and bitmap regions are reused for the sort
@@ -710,6 +753,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     lds_barrier();  // the victim list is rewritten below
   }
 
+  PHASE_POINT(5);
   // Step 5: the victim of rank j takes the j-th miss: its owner sets token,
   // row ID and the device row of plan entry j; the miss's owner writes the
   // host row of plan entry j.  The fused copy keeps the plan's device rows
@@ -754,6 +798,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       if (vict & (1u << j)) st[s0 + j] = sr[j];
     }
   }
+  PHASE_POINT(6);
 
   // Fused miss copy: one wavefront per (layer, miss) row, lane l carrying
   // 16-byte unit l, kCopyRowsInFlight rows in flight per wavefront.  Row
@@ -824,6 +869,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
   if (copy_trips && lane == 0 && p.stats) atomicAdd(&p.stats[4], (unsigned long long)copy_trips);
+  PHASE_POINT(7);
 }
 
 template <int SPT, int KPT>
@@ -893,6 +939,24 @@ hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream) {
     default: return launch_k<16>(p, batch, lds, stream, kpt);
   }
 }
+
+#ifdef HISPARSE_PHASE_TRACE
+hipError_t phase_trace_clear() {
+  void* d = nullptr;
+  hipError_t e = hipGetSymbolAddress(&d, HIP_SYMBOL(g_phase_trace));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemset(d, 0, sizeof(g_phase_trace));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return e;
+}
+
+hipError_t phase_trace_read(uint64_t* host, size_t count) {
+  if (count * sizeof(uint64_t) != sizeof(g_phase_trace)) return hipErrorInvalidValue;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_trace), sizeof(g_phase_trace));
+  return e;
+}
+#endif
 
 hipError_t prepare_resolve(size_t) {
   hipError_t e = set_attr_k<1>();

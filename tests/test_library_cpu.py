@@ -1,5 +1,6 @@
 """CPU checks of the C-ABI library: it builds for gfx950, loads, and exports
-every entry point include/hisparse.h declares (no compute calls)."""
+every entry point include/hisparse.h declares (no compute calls); the
+diagnostic build exports those and the ones of include/hisparse_diag.h."""
 import ctypes
 import os
 import re
@@ -8,10 +9,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hisparse.h")
+DIAG_HEADER = os.path.join(ROOT, "include", "hisparse_diag.h")
+DIAG_LIB = os.path.join(ROOT, "hierarchical_sparse_attention_hisparse_amd", "libhisparse_diag.so")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b(hisparse_[a-z_0-9]+)\s*\(", text)
     return sorted(set(names))
@@ -35,6 +38,25 @@ def test_library_loads_and_exports_every_symbol():
     # the binding loads the same library
     assert hs.load_library() is not None
     assert hs.hisparse_last_error() == ""
+
+
+def test_diagnostic_library_exports_both_headers_and_the_library_only_its_own():
+    import hierarchical_sparse_attention_hisparse_amd as hs
+    from hierarchical_sparse_attention_hisparse_amd.build import build_library
+    if not (os.path.exists(hs.library_path()) and os.path.exists(DIAG_LIB)):
+        build_library(force=True)
+    diag_names = _declared_functions(DIAG_HEADER)
+    assert set(diag_names) == {"hisparse_diag_phase_clear", "hisparse_diag_phase_read",
+                               "hisparse_diag_floor"}
+    diag = ctypes.CDLL(DIAG_LIB)
+    for name in _declared_functions() + diag_names:
+        assert hasattr(diag, name), name
+    lib = ctypes.CDLL(hs.library_path())
+    for name in diag_names:
+        assert not hasattr(lib, name), name
+    data = open(DIAG_LIB, "rb").read()
+    device = [t for t in _offload_bundle_targets(data) if not t.startswith("host-")]
+    assert set(device) == {"hipv4-amdgcn-amd-amdhsa--gfx950"}, device
 
 
 def _offload_bundle_targets(data: bytes):
