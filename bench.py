@@ -514,6 +514,19 @@ def plan_phases(w, g, hs, torch, stream, args):
         torch.cuda.synchronize()
         floors[name] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
     res["floors_us"] = floors
+    # splitting a request over G workgroups: a last-arriver exchange per row
+    # (partials, agent-scope fence, arrival counter), G x batch workgroups
+    xs = torch.zeros((w.B, hs.EXCHANGE_ROW_INTS), dtype=torch.int32, device="cuda")
+    exch = {}
+    for groups in (1, 2, 4, 8):
+        hs.hisparse_diag_exchange(stream, w.B, groups, xs, launches=10)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        hs.hisparse_diag_exchange(stream, w.B, groups, xs, launches=200)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        exch[str(groups)] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
+    res["last_arriver_exchange_us_by_groups"] = exch
     return res
 
 

@@ -12,12 +12,14 @@ plan kernel's phase trace compiled in, plus the diagnostic ones of
 ``include/hisparse_diag.h`` (phase trace, floor kernels).
 """
 from ._binding import (  # noqa: F401
+    EXCHANGE_ROW_INTS,
     HisparseError,
     HostBuffer,
     PoolConfig,
     STAT_NAMES,
     hisparse_decode_layers_overlapped,
     hisparse_destroy_pool,
+    hisparse_diag_exchange,
     hisparse_diag_floor,
     hisparse_diag_phase_clear,
     hisparse_diag_phase_read,

@@ -114,6 +114,8 @@ def load_library():
         lib.hisparse_diag_phase_read.argtypes = [V, ctypes.c_size_t]
         lib.hisparse_diag_floor.restype = I
         lib.hisparse_diag_floor.argtypes = [V, I32, I32, I32, I32, I32, I64, V, V, V, V, V, V, I32]
+        lib.hisparse_diag_exchange.restype = I
+        lib.hisparse_diag_exchange.argtypes = [V, I32, I32, V, I32]
     _lib = lib
     return lib
 
@@ -437,6 +439,7 @@ def hisparse_decode_layers_overlapped(pool, stream, batch, heads, top_k, q_per_l
 
 # ------------------------------------------------- diagnostic library only --
 TRACE_ROWS, TRACE_WAVES, TRACE_POINTS = 256, 16, 9   # include/hisparse_diag.h
+EXCHANGE_ROW_INTS = 64 + 64 * 16
 
 
 def _diag_library():
@@ -475,3 +478,13 @@ def hisparse_diag_floor(stream, kind, batch, top_k=1, slots=1, max_requests=1, m
     _check_rc(_diag_library().hisparse_diag_floor(
         _stream_handle(stream), kind, batch, top_k, slots, max_requests, max_seq_len,
         req, tk, st, lru, locs, op, launches), "hisparse_diag_floor")
+
+
+def hisparse_diag_exchange(stream, batch, groups, scratch, launches=1):
+    """``launches`` back-to-back launches of the last-arriver exchange among
+    ``groups`` workgroups per batch row; ``scratch`` int32 cuda tensor
+    [batch, EXCHANGE_ROW_INTS], zero before the first call."""
+    import torch
+    sp = _dev(scratch, torch.int32, (batch, EXCHANGE_ROW_INTS), "scratch")
+    _check_rc(_diag_library().hisparse_diag_exchange(_stream_handle(stream), batch, groups, sp,
+                                                      launches), "hisparse_diag_exchange")

@@ -92,6 +92,32 @@ __global__ __launch_bounds__(kFloorThreads) void floor_chain_kernel(FloorParams 
   }
 }
 
+// Last-arriver exchange among `groups` workgroups of one batch row: partials
+// written and fenced, the row's counter bumped; the last workgroup reads
+// every partial and resets the counter.  No workgroup waits for another.
+constexpr int kExchangeThreads = 256;
+constexpr int kExchangeMaxGroups = 16;
+static_assert(HISPARSE_EXCHANGE_ROW_INTS == 64 + 64 * kExchangeMaxGroups, "exchange row");
+
+__global__ __launch_bounds__(kExchangeThreads) void exchange_kernel(int32_t* scratch, int groups) {
+  __shared__ int last;
+  const int b = blockIdx.x / groups, g = blockIdx.x - b * groups;
+  const int tid = threadIdx.x;
+  int32_t* row = scratch + (int64_t)b * HISPARSE_EXCHANGE_ROW_INTS;
+  if (tid < 64) row[64 + g * 64 + tid] = g + tid;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&row[0], 1) == groups - 1 ? 1 : 0;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  int s = 0;
+  for (int x = tid; x < groups * 64; x += kExchangeThreads)
+    s += __hip_atomic_load(&row[64 + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 32) row[32 + tid] = s;
+  if (tid == 0) row[0] = 0;
+}
+
 }  // namespace
 }  // namespace hisparse
 
@@ -158,6 +184,24 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return report_error(HISPARSE_EHIP, "floor kernel launch: %s", hipGetErrorString(e));
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_diag_exchange(void* stream, int32_t batch, int32_t groups, int32_t* scratch,
+                           int32_t launches) {
+  if (!scratch) return report_error(HISPARSE_EINVAL, "scratch is NULL");
+  if (groups < 1 || groups > kExchangeMaxGroups)
+    return report_error(HISPARSE_EINVAL, "groups %d not in [1, %d]", groups, kExchangeMaxGroups);
+  if (batch < 1 || (int64_t)batch * groups > 65535)
+    return report_error(HISPARSE_EINVAL, "batch %d * groups %d not in [1, 65535]", batch, groups);
+  if (launches < 1 || launches > (1 << 20))
+    return report_error(HISPARSE_EINVAL, "launches %d not in [1, 1048576]", launches);
+  const hipStream_t s = (hipStream_t)stream;
+  for (int n = 0; n < launches; ++n) {
+    hipLaunchKernelGGL(exchange_kernel, dim3(batch * groups), dim3(kExchangeThreads), 0, s, scratch, groups);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return report_error(HISPARSE_EHIP, "exchange kernel launch: %s", hipGetErrorString(e));
   }
   return HISPARSE_OK;
 }

@@ -88,6 +88,24 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
                         const int32_t* lru_slots, const int64_t* host_cache_locs, int32_t* out,
                         int32_t launches);
 
+/*
+ * The cost of splitting one request over several workgroups: `groups`
+ * workgroups of 256 threads per batch row (grid batch * groups), where each
+ * writes 64 ints of partials, makes them visible device-wide (agent-scope
+ * fence), and bumps its row's arrival counter; the last to arrive reads
+ * every partial of the row, stores their per-thread sums and resets the
+ * counter.  No workgroup waits for another.  `scratch` is device int32
+ * [batch][HISPARSE_EXCHANGE_ROW_INTS]: [0] the arrival counter (zero before
+ * the first call; each call leaves it zero), [32, 64) the sums, [64, ...)
+ * the partials.  Launched `launches` times back to back.  Returns
+ * HISPARSE_EINVAL for a null scratch, 1 <= batch * groups <= 65535 or
+ * 1 <= groups <= 16 violated, or launches outside [1, 1048576];
+ * HISPARSE_EHIP if a launch fails.
+ */
+#define HISPARSE_EXCHANGE_ROW_INTS (64 + 64 * 16)
+int hisparse_diag_exchange(void* stream, int32_t batch, int32_t groups, int32_t* scratch,
+                           int32_t launches);
+
 #ifdef __cplusplus
 }
 #endif

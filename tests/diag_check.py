@@ -123,6 +123,26 @@ def main():
         else:
             raise AssertionError("accepted %s" % bad)
     say("floor kernels compute the stated results; bad kind, batch and launches refused")
+
+    # 4. the last-arriver exchange: sums of every partial, counter left at zero
+    xs = torch.zeros((B, hs.EXCHANGE_ROW_INTS), dtype=torch.int32, device=dev)
+    for groups in (1, 3, 16):
+        hs.hisparse_diag_exchange(None, B, groups, xs, launches=5)
+        torch.cuda.synchronize()
+        x = xs.cpu().numpy()
+        assert (x[:, 0] == 0).all(), "arrival counters not reset"
+        want = np.zeros(32, dtype=np.int64)
+        for t in range(32):
+            want[t] = sum(xx // 64 + xx % 64 for xx in range(t, groups * 64, 256))
+        assert (x[:, 32:64] == want[None, :]).all(), ("exchange sums", groups)
+    for bad in (dict(batch=B, groups=0), dict(batch=B, groups=17), dict(batch=B, groups=2, launches=0)):
+        try:
+            hs.hisparse_diag_exchange(None, scratch=xs, **bad)
+        except hs.HisparseError as e:
+            assert e.code == -1
+        else:
+            raise AssertionError("accepted %s" % bad)
+    say("last-arriver exchange sums every partial and resets its counters")
     print("DIAG OK", flush=True)
 
 
