@@ -550,6 +550,24 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (missbits & (1u << j)) m_entry[mpos++] = i0 + j;
+  int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
+  // The misses' host rows as the fused copy keeps them (see host_row32),
+  // converted for every entry outside any branch, and used by an empty asm
+  // statement: the wait for the host-row loads then sits here on every path,
+  // before the copy's first loads below, and nothing later waits on the
+  // in-order vector-memory counter behind those loads.
+  int32_t h32[KPT];
+  if constexpr (COPY) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      h32[j] = host_row32(hraw[j]);
+      asm volatile("" : : "v"(h32[j]));
+    }
+    int mp = mpos0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (missbits & (1u << j)) m_h[mp++] = h32[j];
+  }
 
   int vr[SPT];  // rank of this slot among the victims, or -1
 #pragma unroll
@@ -558,6 +576,25 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   constexpr int RIF = kCopyRowsInFlight;
   u32x4 pre[RIF];
   bool have_pre = false;
+  // Fused copy, first rows: once the miss list is visible, each wavefront
+  // loads its first kCopyRowsInFlight rows of the first layer, so the host
+  // link works while the victims are ranked and the plan is written; the
+  // rows are stored once their slots are known.  (m_total is uniform.)
+  if (COPY && m_total > 0 && p.units <= kWave) {
+    lds_barrier();
+    have_pre = true;
+#pragma unroll
+    for (int q = 0; q < RIF; ++q) {
+      pre[q] = u32x4{0u, 0u, 0u, 0u};
+      const int j = wid + q * kResolveWaves;
+      if (j < m_total) {
+        const int64_t h = __builtin_amdgcn_readfirstlane(m_h[j]);
+        const bool ok = h >= 0 && h < p.host_rows[0];
+        const gu4* src = ok ? (const gu4*)p.host_pool[0] + h * p.units : (const gu4*)p.zero_row;
+        if (lane < p.units) pre[q] = src[lane];
+      }
+    }
+  }
   const int wrd = s0 >> 6, bit0 = s0 & 63;  // this thread's slots share one bitmap word
 #ifdef HISPARSE_PHASE_TRACE
   int trace_windows = 0;
@@ -615,12 +652,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
               if (rk < need) vr[j] = vbase + rk;
               ++rk;
             }
-          if (COPY && win == 0) {
-            int mp = mpos0;
-#pragma unroll
-            for (int j = 0; j < KPT; ++j)
-              if (missbits & (1u << j)) m_h[mp++] = host_row32(hraw[j]);
-          }
           vbase += need;
           need = 0;
           break;
@@ -628,12 +659,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       }
       // Word prefixes of each key's bitmap (wavefront wid takes keys wid,
       // wid + 16) and the number of candidates of each key.
-      if (COPY && win == 0) {
-        int mp = mpos0;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-          if (missbits & (1u << j)) m_h[mp++] = host_row32(hraw[j]);
-      }
       for (int bin = wid; bin < NBIN; bin += kResolveWaves) {
         uint32_t carry = 0;
         for (int w0 = 0; w0 < W; w0 += kWave) {
@@ -646,24 +671,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         if (lane == 0) scr[kScrBtot + bin] = (int)carry;
       }
       lds_barrier();
-      // Fused copy, first rows: each wavefront loads its first
-      // kCopyRowsInFlight rows of the first layer now (their host rows are
-      // in the miss list), so the host link works while the ranks are
-      // computed; the rows are stored once their slots are known.
-      if (COPY && win == 0 && p.units <= kWave) {
-        have_pre = true;
-#pragma unroll
-        for (int q = 0; q < RIF; ++q) {
-          pre[q] = u32x4{0u, 0u, 0u, 0u};
-          const int j = wid + q * kResolveWaves;
-          if (j < m_total) {
-            const int64_t h = __builtin_amdgcn_readfirstlane(m_h[j]);
-            const bool ok = h >= 0 && h < p.host_rows[0];
-            const gu4* src = ok ? (const gu4*)p.host_pool[0] + h * p.units : (const gu4*)p.zero_row;
-            if (lane < p.units) pre[q] = src[lane];
-          }
-        }
-      }
       const uint32_t bcnt = lane < NBIN ? (uint32_t)scr[kScrBtot + lane] : 0u;
       const uint32_t binc = wave_inclusive_sum(bcnt);
       const int tot = __builtin_amdgcn_readlane((int)binc, 63);
@@ -744,12 +751,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         const int v = vrank[s0 + j];
         if (v >= 0) vr[j] = v;
       }
-    if (COPY && NBIN == 0) {  // the miss list's host rows, not yet written
-      int mp = mpos0;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (missbits & (1u << j)) m_h[mp++] = host_row32(hraw[j]);
-    }
     lds_barrier();  // the victim list is rewritten below
   }
 
@@ -760,7 +761,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // in the victim list (its host rows are the miss list's).  Then every
   // thread writes its slot run back once: stamps of hit and victim slots,
   // tokens of victim slots (vector stores, not one scattered store per slot).
-  int64_t* psrc = p.plan_src + (int64_t)b * p.plan_stride;
   int32_t* pdst = p.plan_dst + (int64_t)b * p.plan_stride;
   unsigned vict = 0;
 #pragma unroll
@@ -776,10 +776,13 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     if (COPY) victim[v] = row;
   }
   {
+    // The plan's host rows.  The fused instance stores the 32-bit values of
+    // its copy list (a row outside [0, 2^31) as -1, out of range for every
+    // pool either way), which wait for no load.
     int mp = mpos0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (missbits & (1u << j)) psrc[mp++] = hraw[j];
+      if (missbits & (1u << j)) psrc[mp++] = COPY ? (int64_t)h32[j] : hraw[j];
   }
   const int32_t c = (int32_t)((uint32_t)clk_now + 1u);
   const unsigned touched = hitm | vict;
