@@ -530,6 +530,57 @@ def plan_phases(w, g, hs, torch, stream, args):
     return res
 
 
+def plan_phases_mixed(hs, torch, stream, reuse, steps):
+    """The plan kernel's phase trace on the mixed-residency workload at one
+    reuse fraction (128 requests, resident tail, 4096 slots, top-2048):
+    step 0 from cold, then `steps` traced plan-only steps.  The plan reads no
+    row bytes, so the host pool is allocated but not filled."""
+    from workloads import config3_mixed_residency, admission
+    dev = torch.device("cuda")
+    w = config3_mixed_residency(reuse)
+    host = hs.HostBuffer(w.host_pool_rows * ROW_BYTES)
+    pools = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)]
+    cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                        row_bytes=w.row_bytes, page_size=w.P, resident_pages=w.resident_pages,
+                        max_seq_len=w.max_seq_len)
+    pool = hs.hisparse_init_pool(cfg, [host], [w.host_pool_rows], pools, w.dev_pool_rows)
+    st0, lru0, clk0, _, _ = admission(w)
+    st, lru, clk = (torch.from_numpy(x).to(dev) for x in (st0, lru0, clk0))
+    locs = torch.from_numpy(w.host_cache_locs).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    req = torch.from_numpy(w.req_idx).to(dev)
+    out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    topk = torch.from_numpy(w.top_k).to(dev)
+    seq = torch.from_numpy(w.seq_lens).to(dev)
+    n = min(steps, w.steps - 1)
+    cyc = rt = 0
+    wins, sorts, n_rows = [], [], 0
+    for i in range(n + 1):
+        hs.hisparse_diag_phase_clear()
+        hs.hisparse_resolve_plan(pool, stream, w.B, w.k, req, topk[i], seq[i], locs, bt, st, lru,
+                                 clk, out, None)
+        torch.cuda.synchronize()
+        if i == 0:
+            continue
+        tr = hs.hisparse_diag_phase_read()
+        rows = np.nonzero(w.seq_lens[i] > w.S)[0]
+        c, r, wi, so, _, _ = phase_summary(tr, rows)
+        cyc, rt = cyc + c, rt + r
+        wins += wi.tolist()
+        sorts += so.tolist()
+        n_rows += len(rows)
+    hs.hisparse_destroy_pool(pool)
+    host.free()
+    return {"workload": "mixed residency, %g reuse: %d requests x %d tokens, last %d resident, "
+                        "%d slots, top-%d; steps 1..%d" % (reuse, w.R, w.max_seq_len,
+                                                           w.resident_pages * w.P // w.R, w.S, w.k, n),
+            "phases": [{"phase": PHASE_NAMES[q], "cycles": round(float(cyc[q]) / n_rows),
+                        "us": round(float(rt[q]) / n_rows / 100.0, 3)} for q in range(7)],
+            "row_total_us": round(float(rt.sum()) / n_rows / 100.0, 3),
+            "windows_per_row": {str(v): wins.count(v) for v in sorted(set(wins))},
+            "sort_fallback_rows": int(sum(sorts))}
+
+
 def host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -636,6 +687,11 @@ def main():
     if args.plan_phases:
         assert hs.is_diag_library()
         res = plan_phases(w, g, hs, torch, stream, args)
+        if not args.no_mixed_residency:
+            del g
+            torch.cuda.empty_cache()
+            res["mixed_residency"] = [plan_phases_mixed(hs, torch, stream, f, min(args.steps, 31))
+                                      for f in (0.99, 0.5)]
         res.update({"metric": "plan kernel phases and floors", "n_gpus": 1, "steps": args.steps,
                     "warmup": args.warmup,
                     "config": {"workload": "dsa_decode: 64 rows of 32768-131072 tokens + 8 "

@@ -208,9 +208,11 @@ constexpr int bits_for(int v) { return v <= 1 ? 1 : 1 + bits_for(v >> 1); }
 __device__ inline int32_t host_row32(int64_t h) { return (h >= 0 && h <= INT_MAX) ? (int32_t)h : -1; }
 
 // Scratch buffers of the call sites, in ints: per-wave partials (16 each)
-// and the window's candidate count per key.
+// and the window's candidate count per key.  kScrKey0 shares the fast path's
+// ints: a row takes one path or the other.
 enum : int {
   kScrFast = 0,
+  kScrKey0 = 0,          // candidates at each wave's smallest key (step 3)
   kScrMiss = 16,
   kScrStats = 32,        // 3 x 16
   kScrMin = 80,          // 2 x 16 u64 (= 64 ints), 8-byte aligned: double-buffered per window
@@ -499,6 +501,11 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
   int mpre;  // misses in lower lanes of this wavefront
+  // This thread's candidates holding the wavefront's smallest key, and how
+  // many such candidates lower lanes hold: if the row's smallest key covers
+  // every miss, they give the ranks with no window at all.
+  unsigned at0w = 0;
+  uint64_t kmw;
   {
     const int a0 = wave_sum_small<bits_for(KPT)>(n_hit);
     const int a1 = wave_sum_small<bits_for(KPT)>(n_res);
@@ -512,11 +519,16 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       wt += __popcll(m) << q;
     }
     const uint64_t km = wave_min_key(kmine);
+    kmw = km;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) at0w |= (((cand >> j) & 1u) && key[j] == km ? 1u : 0u) << j;
+    const int wt0 = wave_sum_small<bits_for(SPT)>(__popc(at0w));
     if (lane == 0) {
       scr[kScrStats + wid] = a0;
       scr[kScrStats + 16 + wid] = a1;
       scr[kScrStats + 32 + wid] = a2;
       scr[kScrMiss + wid] = wt;
+      scr[kScrKey0 + wid] = wt0;
       ((uint64_t*)(scr + kScrMin))[wid] = km;
     }
   }
@@ -599,6 +611,33 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #ifdef HISPARSE_PHASE_TRACE
   int trace_windows = 0;
 #endif
+  uint64_t base0 = 0;  // the row's smallest key (the first window's base)
+  if (need > 0) {
+    // The row's smallest key: if its candidates cover every miss, their
+    // slot order is the victim order (no window, no bitmap).  Waves whose
+    // own smallest key is larger hold none of them.  (Uniform decision.)
+    const uint64_t kp = lane < kResolveWaves ? ((const uint64_t*)(scr + kScrMin))[lane] : ~0ull;
+    const uint64_t base = wave_min_key(kp);
+    base0 = base;
+    const uint32_t inc = wave_inclusive_sum(
+        lane < kResolveWaves && kp == base ? (uint32_t)scr[kScrKey0 + lane] : 0u);
+    if (__builtin_amdgcn_readlane((int)inc, 63) >= need) {
+      if (kmw == base) {
+        const int c0 = __popc(at0w);
+        int rk = wid > 0 ? __builtin_amdgcn_readlane((int)inc, wid - 1) : 0;
+#pragma unroll
+        for (int q = 0; q < bits_for(SPT); ++q) rk += lane_prefix(__ballot((c0 >> q) & 1)) << q;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j)
+          if (at0w & (1u << j)) {
+            if (rk < need) vr[j] = rk;
+            ++rk;
+          }
+      }
+      vbase = need;
+      need = 0;
+    }
+  }
   if (NBIN > 0 && need > 0) {
 #pragma unroll 1
     for (int win = 0;; ++win) {
@@ -609,7 +648,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       // the other half holds the next window's minima only after two more
       // barriers; until then it takes this window's per-wave counts below
       int* key0_part = scr + kScrMin + 32 * ((win + 1) & 1);
-      const uint64_t base = wave_min_key(lane < kResolveWaves ? kmin_part[lane] : ~0ull);
+      // (the first window's base and smallest-key test were done above)
+      const uint64_t base = win == 0 ? base0 : wave_min_key(lane < kResolveWaves ? kmin_part[lane] : ~0ull);
       unsigned inwin = 0, at0 = 0;
       int dd[SPT];
 #pragma unroll
@@ -626,11 +666,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       // they cover every remaining miss, their slot-order prefix is the rank
       // and the window needs no word prefixes (a few misses, as on steps
       // with high reuse).
-      int pre0;
-      {
+      int pre0 = 0;
+      if (win > 0) {
         const int c0 = __popc(at0);
         int wt = 0;
-        pre0 = 0;
 #pragma unroll
         for (int q = 0; q < bits_for(SPT); ++q) {
           const uint64_t m = __ballot((c0 >> q) & 1);
@@ -640,7 +679,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
         if (lane == 0) key0_part[wid] = wt;
       }
       lds_barrier();
-      {
+      if (win > 0) {
         const uint32_t k0 = lane < kResolveWaves ? (uint32_t)key0_part[lane] : 0u;
         const uint32_t inc0 = wave_inclusive_sum(k0);
         const int tot0 = __builtin_amdgcn_readlane((int)inc0, 63);

@@ -42,7 +42,8 @@ extern "C" {
  *   5 victims ranked (step 4: windows, or the sort fallback);
  *   6 plan, row IDs and slot state written (step 5);
  *   7 end of the workgroup (after the fused copy in the fused instance).
- * Point 8 holds [0] the ranking windows used and [1] 1 if the sort fallback
+ * Point 8 holds [0] the ranking windows used (0: no miss, or the row's
+ * smallest key alone covered every miss) and [1] 1 if the sort fallback
  * ran.  Rows that take the fast path (seq_len <= slots) or are padding
  * return after point 0.  The trace of a launch overwrites the one before;
  * points a launch does not reach keep what was there, so clear between

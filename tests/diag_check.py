@@ -30,13 +30,15 @@ def say(*a):
 def check_trace(tr, long_rows, other_rows):
     """Every wavefront of a long row passed points 0-7; the row's points are
     reached in order (last wavefront, real-time counter); other rows stop at
-    point 0; the info point names at least one window or the sort."""
+    point 0; the info point holds at most 4 windows and a 0/1 sort flag, the
+    same in every wavefront."""
     for b in long_rows:
         t = tr[b]
         assert (t[:, :8, :] > 0).all(), "row %d: a phase point was not reached" % b
         last = t[:, :8, 1].astype(np.int64).max(axis=0)
         assert (np.diff(last) >= 0).all(), ("row %d: points out of order" % b, last)
-        assert t[0, 8, 0] >= 1 or t[0, 8, 1] == 1, "row %d: no ranking recorded" % b
+        assert t[0, 8, 0] <= 4 and t[0, 8, 1] in (0, 1), ("row %d: ranking info" % b, t[0, 8])
+        assert (t[:, 8, :] == t[0, 8, :]).all(), "row %d: wavefronts disagree on the ranking" % b
     for b in other_rows:
         assert (tr[b, :, 1:8, :] == 0).all(), "row %d (fast path): points past 0 written" % b
         assert (tr[b, :, 0, :] > 0).all(), "row %d: entry not recorded" % b
