@@ -514,6 +514,23 @@ def plan_phases(w, g, hs, torch, stream, args):
         torch.cuda.synchronize()
         floors[name] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
     res["floors_us"] = floors
+    # hit detection alone, both ways round (same probing, same launch shape)
+    hit, outs = {}, []
+    for mode, name in ((0, "positions_table_probed_by_slots"), (1, "slot_map_probed_by_entries")):
+        o = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+        fn = lambda n, mode=mode, o=o: hs.hisparse_diag_hit_detection(
+            stream, mode, w.B, w.k, w.S, w.R, w.max_seq_len, g["req"], g["topk"][i_last],
+            g["seq"][i_last], g["st"], o, launches=n)
+        fn(10)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn(200)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hit[name] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
+        outs.append(o)
+    hit["same_result"] = bool(torch.equal(outs[0], outs[1]))
+    res["hit_detection_us"] = hit
     # splitting a request over G workgroups: a last-arriver exchange per row
     # (partials, agent-scope fence, arrival counter), G x batch workgroups
     xs = torch.zeros((w.B, hs.EXCHANGE_ROW_INTS), dtype=torch.int32, device="cuda")

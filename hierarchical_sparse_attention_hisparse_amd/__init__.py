@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     hisparse_destroy_pool,
     hisparse_diag_exchange,
     hisparse_diag_floor,
+    hisparse_diag_hit_detection,
     hisparse_diag_phase_clear,
     hisparse_diag_phase_read,
     hisparse_gather_copy,

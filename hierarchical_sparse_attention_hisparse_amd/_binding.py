@@ -114,6 +114,8 @@ def load_library():
         lib.hisparse_diag_phase_read.argtypes = [V, ctypes.c_size_t]
         lib.hisparse_diag_floor.restype = I
         lib.hisparse_diag_floor.argtypes = [V, I32, I32, I32, I32, I32, I64, V, V, V, V, V, V, I32]
+        lib.hisparse_diag_hit_detection.restype = I
+        lib.hisparse_diag_hit_detection.argtypes = [V, I32, I32, I32, I32, I32, I64, V, V, V, V, V, I32]
         lib.hisparse_diag_exchange.restype = I
         lib.hisparse_diag_exchange.argtypes = [V, I32, I32, V, I32]
     _lib = lib
@@ -488,3 +490,18 @@ def hisparse_diag_exchange(stream, batch, groups, scratch, launches=1):
     sp = _dev(scratch, torch.int32, (batch, EXCHANGE_ROW_INTS), "scratch")
     _check_rc(_diag_library().hisparse_diag_exchange(_stream_handle(stream), batch, groups, sp,
                                                       launches), "hisparse_diag_exchange")
+
+
+def hisparse_diag_hit_detection(stream, mode, batch, top_k, slots, max_requests, max_seq_len,
+                                req_idx, top_k_tokens, seq_lens, slot_tokens, out, launches=1):
+    """Hit detection alone (mode 0: positions table probed by the slots; mode 1:
+    slot -> token map probed by the entries); ``out`` int32 [batch, top_k]."""
+    import torch
+    rp = _dev(req_idx, torch.int32, (batch,), "req_idx")
+    tp = _dev(top_k_tokens, torch.int32, (batch, top_k), "top_k_tokens")
+    sp = _dev(seq_lens, torch.int32, (batch,), "seq_lens")
+    stp = _dev(slot_tokens, torch.int32, (max_requests, slots), "slot_tokens")
+    op = _dev(out, torch.int32, (batch, top_k), "out")
+    _check_rc(_diag_library().hisparse_diag_hit_detection(
+        _stream_handle(stream), mode, batch, top_k, slots, max_requests, max_seq_len, rp, tp, sp,
+        stp, op, launches), "hisparse_diag_hit_detection")

@@ -92,6 +92,110 @@ __global__ __launch_bounds__(kFloorThreads) void floor_chain_kernel(FloorParams 
   }
 }
 
+// Hit detection alone, both ways round, one 1024-thread workgroup per batch
+// row, with the same single-cell linear probing and 4 table cells per
+// inserted item in both: out[b][i] = the lowest slot of the request holding
+// entry i's position, or -1.
+//   MODE 0: the entries' positions go into the table (top-k index per cell)
+//           and every slot probes it with its token (the library's way);
+//   MODE 1: the slots' tokens go into the table (lowest slot per cell) and
+//           every entry probes it with its position (a slot -> token map).
+constexpr int kHitMaxK = 4096, kHitMaxS = 4096;
+
+__device__ inline uint32_t hit_hash(int t, int shift) { return ((uint32_t)t * 2654435761u) >> shift; }
+
+struct HitParams {
+  int32_t k, S, R;
+  int64_t max_seq_len;
+  const int32_t* req;
+  const int32_t* topk;
+  const int32_t* seq;
+  const int32_t* st;
+  int32_t* out;
+  int32_t cells, shift;  // table cells (power of two) and hash shift
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kFloorThreads) void hit_detect_kernel(HitParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* key = (int32_t*)smem;           // [cells]: position / token, -1 = free
+  int32_t* val = key + p.cells;            // [cells]: MODE 0 top-k index, MODE 1 lowest slot
+  int32_t* ehit = val + p.cells;           // MODE 0: [k] lowest hit slot per entry
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int r = clamp_req(p.req[b], p.R);
+  const int64_t n = p.seq[b] < p.max_seq_len ? (int64_t)p.seq[b] : p.max_seq_len;
+  const int32_t* tk = p.topk + (int64_t)b * p.k;
+  const int32_t* st = p.st + (int64_t)r * p.S;
+  const int mask = p.cells - 1;
+  for (int x = tid; x < p.cells; x += kFloorThreads) {
+    key[x] = -1;
+    val[x] = INT_MAX;
+  }
+  if (MODE == 0)
+    for (int i = tid; i < p.k; i += kFloorThreads) ehit[i] = INT_MAX;
+  __syncthreads();
+  if (MODE == 0) {
+    for (int i = tid; i < p.k; i += kFloorThreads) {
+      const int t = tk[i];
+      if (t < 0 || (int64_t)t >= n) continue;
+      uint32_t h = hit_hash(t, p.shift);
+      while (true) {
+        const int prev = atomicCAS(&key[h], -1, t);
+        if (prev == -1) {
+          val[h] = i;
+          break;
+        }
+        if (prev == t) break;
+        h = (h + 1) & mask;
+      }
+    }
+    __syncthreads();
+    for (int s = tid; s < p.S; s += kFloorThreads) {
+      const int tok = st[s];
+      if (tok < 0 || (int64_t)tok >= n) continue;
+      for (uint32_t h = hit_hash(tok, p.shift);; h = (h + 1) & mask) {
+        const int c = key[h];
+        if (c == tok) {
+          atomicMin(&ehit[val[h]], s);
+          break;
+        }
+        if (c == -1) break;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < p.k; i += kFloorThreads)
+      p.out[(int64_t)b * p.k + i] = ehit[i] == INT_MAX ? -1 : ehit[i];
+  } else {
+    for (int s = tid; s < p.S; s += kFloorThreads) {
+      const int tok = st[s];
+      if (tok < 0 || (int64_t)tok >= n) continue;
+      for (uint32_t h = hit_hash(tok, p.shift);; h = (h + 1) & mask) {
+        const int prev = atomicCAS(&key[h], -1, tok);
+        if (prev == -1 || prev == tok) {
+          atomicMin(&val[h], s);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < p.k; i += kFloorThreads) {
+      const int t = tk[i];
+      int res = -1;
+      if (t >= 0 && (int64_t)t < n) {
+        for (uint32_t h = hit_hash(t, p.shift);; h = (h + 1) & mask) {
+          const int c = key[h];
+          if (c == t) {
+            res = val[h];
+            break;
+          }
+          if (c == -1) break;
+        }
+      }
+      p.out[(int64_t)b * p.k + i] = res;
+    }
+  }
+}
+
 // Last-arriver exchange among `groups` workgroups of one batch row: partials
 // written and fenced, the row's counter bumped; the last workgroup reads
 // every partial and resets the counter.  No workgroup waits for another.
@@ -184,6 +288,46 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return report_error(HISPARSE_EHIP, "floor kernel launch: %s", hipGetErrorString(e));
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_diag_hit_detection(void* stream, int32_t mode, int32_t batch, int32_t top_k, int32_t slots,
+                                int32_t max_requests, int64_t max_seq_len, const int32_t* req_idx,
+                                const int32_t* top_k_tokens, const int32_t* seq_lens,
+                                const int32_t* slot_tokens, int32_t* out, int32_t launches) {
+  if (mode < 0 || mode > 1) return report_error(HISPARSE_EINVAL, "mode %d not in [0, 1]", mode);
+  if (batch < 1 || batch > 65535) return report_error(HISPARSE_EINVAL, "batch %d not in [1, 65535]", batch);
+  if (top_k < 1 || top_k > kHitMaxK)
+    return report_error(HISPARSE_EINVAL, "top_k %d not in [1, %d]", top_k, kHitMaxK);
+  if (slots < 1 || slots > kHitMaxS)
+    return report_error(HISPARSE_EINVAL, "slots %d not in [1, %d]", slots, kHitMaxS);
+  if (max_requests < 1 || max_seq_len < 1)
+    return report_error(HISPARSE_EINVAL, "max_requests %d or max_seq_len %lld < 1", max_requests,
+                        (long long)max_seq_len);
+  if (!req_idx || !top_k_tokens || !seq_lens || !slot_tokens || !out)
+    return report_error(HISPARSE_EINVAL, "a device array is NULL");
+  if (launches < 1 || launches > (1 << 20))
+    return report_error(HISPARSE_EINVAL, "launches %d not in [1, 1048576]", launches);
+  const int items = mode == 0 ? top_k : slots;
+  int cells = 64;
+  while (cells < 4 * items) cells <<= 1;
+  int lg = 0;
+  while ((1 << lg) < cells) ++lg;
+  HitParams p{top_k, slots, max_requests, max_seq_len, req_idx, top_k_tokens, seq_lens, slot_tokens,
+              out, cells, 32 - lg};
+  const size_t lds = (size_t)2 * cells * sizeof(int32_t) + (mode == 0 ? (size_t)top_k * sizeof(int32_t) : 0);
+  const void* fn = mode == 0 ? (const void*)hit_detect_kernel<0> : (const void*)hit_detect_kernel<1>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return report_error(HISPARSE_EHIP, "hit detection set-up: %s", hipGetErrorString(e));
+  const hipStream_t s = (hipStream_t)stream;
+  for (int n = 0; n < launches; ++n) {
+    if (mode == 0)
+      hipLaunchKernelGGL(hit_detect_kernel<0>, dim3(batch), dim3(kFloorThreads), lds, s, p);
+    else
+      hipLaunchKernelGGL(hit_detect_kernel<1>, dim3(batch), dim3(kFloorThreads), lds, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return report_error(HISPARSE_EHIP, "hit detection launch: %s", hipGetErrorString(e));
   }
   return HISPARSE_OK;
 }

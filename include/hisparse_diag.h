@@ -90,6 +90,30 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
                         int32_t launches);
 
 /*
+ * Hit detection alone, both ways round, for a measured comparison: one
+ * 1024-thread workgroup per batch row on `stream`, the same single-cell
+ * linear probing and 4 table cells per inserted item either way.
+ * out[b][i] (int32 [batch][top_k]) = the lowest slot s of request
+ * req_idx[b] (clamped to [0, max_requests)) with slot_tokens[r][s] equal to
+ * entry i's position, or -1 (also for positions outside
+ * [0, min(seq_lens[b], max_seq_len))).  `mode`:
+ *   0 the entries' positions go into an LDS table and every slot probes it
+ *     with its token (the plan kernel's direction);
+ *   1 the slots' tokens go into an LDS table (a slot -> token map, lowest
+ *     slot per token) and every entry probes it with its position.
+ * Positions within a row must be distinct, as for hisparse_resolve.
+ * Launched `launches` times back to back.  Returns HISPARSE_EINVAL for a bad
+ * mode, a NULL array, 1 <= batch <= 65535, 1 <= top_k <= 4096,
+ * 1 <= slots <= 4096, max_requests or max_seq_len < 1, or launches outside
+ * [1, 1048576]; HISPARSE_EHIP if a launch fails.
+ */
+int hisparse_diag_hit_detection(void* stream, int32_t mode, int32_t batch, int32_t top_k,
+                                int32_t slots, int32_t max_requests, int64_t max_seq_len,
+                                const int32_t* req_idx, const int32_t* top_k_tokens,
+                                const int32_t* seq_lens, const int32_t* slot_tokens, int32_t* out,
+                                int32_t launches);
+
+/*
  * The cost of splitting one request over several workgroups: `groups`
  * workgroups of 256 threads per batch row (grid batch * groups), where each
  * writes 64 ints of partials, makes them visible device-wide (agent-scope

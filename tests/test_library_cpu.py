@@ -47,7 +47,8 @@ def test_diagnostic_library_exports_both_headers_and_the_library_only_its_own():
         build_library(force=True)
     diag_names = _declared_functions(DIAG_HEADER)
     assert set(diag_names) == {"hisparse_diag_phase_clear", "hisparse_diag_phase_read",
-                               "hisparse_diag_floor", "hisparse_diag_exchange"}
+                               "hisparse_diag_floor", "hisparse_diag_exchange",
+                               "hisparse_diag_hit_detection"}
     diag = ctypes.CDLL(DIAG_LIB)
     for name in _declared_functions() + diag_names:
         assert hasattr(diag, name), name
