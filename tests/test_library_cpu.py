@@ -171,6 +171,43 @@ def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
     assert res.stdout.startswith("-1 ") and "NULL" in res.stdout
 
 
+def test_diagnostic_header_is_plain_c_and_links_from_c(tmp_path):
+    """include/hisparse_diag.h compiles as strict C99 (with hisparse.h) and as
+    C++17; a C program links libhisparse_diag.so and gets the stated refusal
+    back from diagnostic calls with bad arguments (no GPU needed)."""
+    import shutil
+    import subprocess
+    from hierarchical_sparse_attention_hisparse_amd.build import build_library
+    if shutil.which("gcc") is None or shutil.which("g++") is None:
+        pytest.skip("no host C/C++ compiler")
+    if not os.path.exists(DIAG_LIB):
+        build_library(force=True)
+    inc = os.path.join(ROOT, "include")
+    libdir = os.path.dirname(DIAG_LIB)
+    src = tmp_path / "use_diag.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "hisparse.h"\n#include "hisparse_diag.h"\n'
+        "int main(void) {\n"
+        "  uint64_t w[1];\n"
+        "  int a = hisparse_diag_phase_read(w, 1);\n"
+        "  int b = hisparse_diag_floor(NULL, 9, 1, 1, 1, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, 1);\n"
+        "  int c = hisparse_diag_exchange(NULL, 1, 0, NULL, 1);\n"
+        "  int d = hisparse_diag_hit_detection(NULL, 2, 1, 1, 1, 1, 1, NULL, NULL, NULL, NULL, NULL, 1);\n"
+        '  printf("%d %d %d %d %d %s\\n", a, b, c, d, HISPARSE_TRACE_WORDS, hisparse_last_error());\n'
+        "  return a == HISPARSE_EINVAL && b == HISPARSE_EINVAL && c == HISPARSE_EINVAL &&\n"
+        "         d == HISPARSE_EINVAL ? 0 : 1;\n"
+        "}\n")
+    exe = tmp_path / "use_diag"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", inc,
+                    str(src), "-L", libdir, "-l:libhisparse_diag.so", "-Wl,-rpath," + libdir,
+                    "-o", str(exe)], check=True)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++", "-I", inc,
+                    str(src)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.startswith("-1 -1 -1 -1 73728 "), res.stdout
+
+
 def _init_rc(cfg_kwargs, device_pool_rows=None, layer0=None):
     """hisparse_init_pool through the C ABI.  The pool arrays are NULL unless
     `layer0` = (host pointer, host rows, device pointer) is given; those
