@@ -11,7 +11,8 @@ constexpr int kWave = 64;
 
 // Launch shapes and LDS limits of the resolver.
 constexpr int kResolveThreads = 1024;  // threads per request row
-constexpr int kHashFactor = 4;         // table cells per top-k entry
+constexpr int kHashFactor = 8;         // table cells per top-k entry
+constexpr int kBucketCells = 8;        // cells per bucket of the table (the probe's read)
 constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxSlots = 16384;
@@ -64,11 +65,11 @@ __host__ __device__ inline int ilog2(int v) {
 constexpr int kResolveScratchInts = 176;
 
 struct ResolveLds {
-  int hash_size;   // cells of the table (power of two >= 2k)
+  int hash_size;   // cells of the table (power of two >= 2k, >= 64)
   int sort_size;   // power of two >= S (fallback sort)
   int words;       // 64-bit words of one slot bitmap: ceil(S / 64)
   int bins;        // keys ranked per window (<= kMaxRankBins), 0 = sort only
-  size_t off_hash, off_hidx, off_ehit, off_sort, off_bits, off_wpre;
+  size_t off_hash, off_hidx, off_hcnt, off_ehit, off_sort, off_bits, off_wpre;
   size_t off_etok, off_mentry, off_mhost, off_victim, off_scratch;
   size_t total;
 };
@@ -91,7 +92,8 @@ __host__ __device__ inline ResolveLds resolve_lds_layout_f(int S, int k, int fac
   size_t o = 0;
   L.off_hash = o;                                               // int32 positions
   L.off_hidx = align16(L.off_hash + 4 * (size_t)L.hash_size);   // uint16 top-k indices
-  L.off_ehit = align16(L.off_hidx + 2 * (size_t)L.hash_size);
+  L.off_hcnt = align16(L.off_hidx + 2 * (size_t)L.hash_size);   // int32 fill count per bucket
+  L.off_ehit = align16(L.off_hcnt + 4 * (size_t)(L.hash_size / kBucketCells));
   const size_t end_hash = align16(L.off_ehit + 4 * (size_t)k);
   L.off_sort = o;
   const size_t end_sort = align16(L.off_sort + 8 * (size_t)L.sort_size);

@@ -4,9 +4,9 @@
 // a contiguous run of SPT slots and a contiguous run of KPT top-k entries, so
 // "ascending slot" and "ascending top-k index" are thread order.  Slot tokens
 // and stamps stay in registers; LDS holds an open-addressing table of the
-// pending positions (one 64-bit word per cell: position << 32 | top-k index),
-// the per-entry hit slot, the miss list, the victim ranking's bitmaps and
-// per-wave partials.  Steps:
+// pending positions (32-bit cells in buckets of 8, with each cell's top-k
+// index in a parallel 16-bit array), the per-entry hit slot, the miss list,
+// the victim ranking's bitmaps and per-wave partials.  Steps:
 //   1. validity and the resident short-circuit; pending positions are
 //      inserted into the table;
 //   2. each slot holding a pending position marks that entry's hit slot (the
@@ -321,6 +321,13 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int vzero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
   const int32_t clk_now = p.clk[r + vzero];
+  // The fill-count increment of step 1, in a register defined before the
+  // block-table loads below: were it placed after them, it could share a
+  // register with one of those loads, and the rows without a block table
+  // would then wait for every load in flight (slot state included) before
+  // their inserts.
+  int vone;
+  asm volatile("v_mov_b32 %0, 1" : "=v"(vone));
 
   // Block-table entries of this thread's positions, at in-range indices,
   // issued with the slot-state loads so that both round trips overlap.
@@ -335,16 +342,17 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
   }
 
-  // Table of the pending positions: linear probing over 32-bit cells (a
-  // position, -1 = empty), with the top-k index of each cell in a parallel
-  // 16-bit array.  Inserts take the first free cell from the position's
-  // hash with one compare-and-swap per step; probes read the cells in
-  // aligned groups of four (16 bytes), stop at the first match or free cell,
-  // and read the matched cell's index once, after their loop.  Cells are
-  // never freed within a call, so every cell between a position's hash and
-  // its own is taken.
+  // Table of the pending positions: 32-bit cells (a position, -1 = empty)
+  // in buckets of kBucketCells, with the top-k index of each cell in a
+  // parallel 16-bit array.  A position hashes to a bucket and takes the cell
+  // that the bucket's fill count names (one atomic add); past a full bucket
+  // it tries the next.  So the taken cells of a bucket are a prefix of it,
+  // and a position absent from a bucket whose last cell is free is absent
+  // from the table.  Probes read whole buckets (two 16-byte reads) and read
+  // the matched cell's index once, after their loop.
   int32_t* Hc = (int32_t*)(smem + L.off_hash);
   uint16_t* Hi = (uint16_t*)(smem + L.off_hidx);
+  int32_t* Hn = (int32_t*)(smem + L.off_hcnt);
   int32_t* e_hit = (int32_t*)(smem + L.off_ehit);
   int32_t* e_tok = (int32_t*)(smem + L.off_etok);
   int32_t* m_entry = (int32_t*)(smem + L.off_mentry);
@@ -353,9 +361,11 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int32_t* m_h = (int32_t*)(smem + L.off_mhost);
   uint64_t* s_sort = (uint64_t*)(smem + L.off_sort);
   const int HS = L.hash_size;
-  const int hshift = 32 - ilog2(HS);
+  const int NBK = HS / kBucketCells;        // buckets (a power of two >= 8)
+  const int bshift = 32 - ilog2(NBK);
 
   for (int x = tid; x < HS / 4; x += kResolveThreads) ((i32x4*)Hc)[x] = i32x4{-1, -1, -1, -1};
+  for (int x = tid; x < NBK / 4; x += kResolveThreads) ((i32x4*)Hn)[x] = i32x4{0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (i0 + j < k) e_hit[i0 + j] = INT_MAX;
@@ -365,9 +375,12 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // through step 1 and the row-ID and stamp stores never hold a barrier.
   lds_barrier();
 
-  // Step 1: validity, resident pages, table of pending positions.
+  // Step 1: validity, resident pages, table of pending positions.  A
+  // thread's inserts issue their fill-count adds together.
   int n_res = 0, n_trip = 0;
   unsigned pend = 0;
+  uint32_t ibk[KPT];
+  int icell[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = i0 + j;
@@ -388,38 +401,44 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
     }
     pend |= 1u << j;
     e_tok[i] = t;
-    uint32_t h = hash_pos(t, hshift);
-    while (true) {
-      const int prev = atomicCAS(&Hc[h], -1, t);
-      if (prev == -1) {
-        Hi[h] = (uint16_t)i;
-        break;
-      }
-      if (prev == t) break;  // a repeat
-      h = (h + 1) & (HS - 1);
+    ibk[j] = hash_pos(t, bshift);
+    icell[j] = atomicAdd(&Hn[ibk[j]], vone);
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (!((pend >> j) & 1u)) continue;
+    // a full bucket: the next one (the table has at least twice as many
+    // cells as entries, so a bucket with room is always reached)
+    while (icell[j] >= kBucketCells) {
+      ibk[j] = (ibk[j] + 1) & (NBK - 1);
+      icell[j] = atomicAdd(&Hn[ibk[j]], vone);
     }
+    const int cell = (int)ibk[j] * kBucketCells + icell[j];
+    Hc[cell] = tr[j];
+    Hi[cell] = (uint16_t)(i0 + j);
   }
   PHASE_POINT(2);
   lds_barrier();
 
   // Step 2: probe the table with every slot's token; the SPT probes of a
-  // thread advance together (their first groups read back to back), so a
-  // wavefront waits for its longest chain once.  Cells of a group below the
-  // probe's start are skipped (-2: neither free nor a position).
+  // thread advance together (their first buckets read back to back), so a
+  // wavefront waits for its longest chain once.  A position is in the table
+  // once per pending entry that holds it, so at most one cell matches unless
+  // the row repeats a position (outside the contract): then the matched cell
+  // may be wrong, and the index check below keeps every access in range.
   int hidx[SPT];  // top-k index of the pending entry this slot's token matches, or -1
   {
-    uint32_t g[SPT], o[SPT];
-    i32x4 v[SPT];
+    uint32_t g[SPT];
+    i32x4 va[SPT], vb[SPT];
     int hcell[SPT];  // table cell holding this slot's token, or -1
     unsigned live = 0;
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int tok = sr[j];
       if ((s0 + j < S) && tok >= 0 && (int64_t)tok < n) live |= 1u << j;
-      const uint32_t h = hash_pos(tok, hshift);  // in range for any token
-      g[j] = h >> 2;
-      o[j] = h & 3;
-      v[j] = ((const i32x4*)Hc)[g[j]];
+      g[j] = hash_pos(tok, bshift);  // in range for any token
+      va[j] = ((const i32x4*)Hc)[2 * g[j]];
+      vb[j] = ((const i32x4*)Hc)[2 * g[j] + 1];
       hcell[j] = -1;
     }
     while (true) {
@@ -427,26 +446,30 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
       for (int j = 0; j < SPT; ++j) {
         const int tok = sr[j];
-        const int c0 = o[j] <= 0 ? v[j].x : -2, c1 = o[j] <= 1 ? v[j].y : -2;
-        const int c2 = o[j] <= 2 ? v[j].z : -2, c3 = v[j].w;
-        const int q = c0 == tok ? 0 : c1 == tok ? 1 : c2 == tok ? 2 : c3 == tok ? 3 : 4;
-        const bool fr = (c0 == -1) | (c1 == -1) | (c2 == -1) | (c3 == -1);
+        const bool m0 = va[j].x == tok, m1 = va[j].y == tok, m2 = va[j].z == tok, m3 = va[j].w == tok;
+        const bool m4 = vb[j].x == tok, m5 = vb[j].y == tok, m6 = vb[j].z == tok, m7 = vb[j].w == tok;
+        const bool any = m0 | m1 | m2 | m3 | m4 | m5 | m6 | m7;
+        const int q = ((m1 | m3 | m5 | m7) ? 1 : 0) | ((m2 | m3 | m6 | m7) ? 2 : 0) |
+                      ((m4 | m5 | m6 | m7) ? 4 : 0);
         const bool lj = (live >> j) & 1u;
-        hcell[j] = (lj && q < 4) ? (int)(4 * g[j]) + q : hcell[j];
-        next |= (lj && q == 4 && !fr) ? 1u << j : 0u;  // no match, no free cell: next group
+        hcell[j] = (lj && any) ? (int)(kBucketCells * g[j]) + q : hcell[j];
+        next |= (lj && !any && vb[j].w != -1) ? 1u << j : 0u;  // full bucket, no match: the next one
       }
       if (next == 0) break;
       live = next;
 #pragma unroll
       for (int j = 0; j < SPT; ++j) {
         const bool nj = (next >> j) & 1u;
-        g[j] = nj ? (g[j] + 1) & (HS / 4 - 1) : g[j];
-        o[j] = nj ? 0 : o[j];
-        v[j] = ((const i32x4*)Hc)[g[j]];
+        g[j] = nj ? (g[j] + 1) & (NBK - 1) : g[j];
+        va[j] = ((const i32x4*)Hc)[2 * g[j]];
+        vb[j] = ((const i32x4*)Hc)[2 * g[j] + 1];
       }
     }
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) hidx[j] = hcell[j] >= 0 ? (int)Hi[hcell[j] >= 0 ? hcell[j] : 0] : -1;
+    for (int j = 0; j < SPT; ++j) {
+      const int x = hcell[j] >= 0 ? (int)Hi[hcell[j] >= 0 ? hcell[j] : 0] : -1;
+      hidx[j] = x < k ? x : -1;
+    }
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
       if (hidx[j] >= 0) atomicMin(&e_hit[hidx[j]], s0 + j);
