@@ -12,7 +12,7 @@ constexpr int kWave = 64;
 // Launch shapes and LDS limits of the resolver.
 constexpr int kResolveThreads = 1024;  // threads per request row
 constexpr int kHashFactor = 8;         // table cells per top-k entry
-constexpr int kBucketCells = 8;        // cells per bucket of the table (the probe's read)
+constexpr int kBucketCells = 4;        // cells per bucket of the table (the probe's read)
 constexpr int kResolveWaves = kResolveThreads / kWave;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxSlots = 16384;

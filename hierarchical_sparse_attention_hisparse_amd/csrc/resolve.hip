@@ -4,7 +4,7 @@
 // a contiguous run of SPT slots and a contiguous run of KPT top-k entries, so
 // "ascending slot" and "ascending top-k index" are thread order.  Slot tokens
 // and stamps stay in registers; LDS holds an open-addressing table of the
-// pending positions (32-bit cells in buckets of 8, with each cell's top-k
+// pending positions (32-bit cells in buckets of 4, with each cell's top-k
 // index in a parallel 16-bit array), the per-entry hit slot, the miss list,
 // the victim ranking's bitmaps and per-wave partials.  Steps:
 //   1. validity and the resident short-circuit; pending positions are
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // that the bucket's fill count names (one atomic add); past a full bucket
   // it tries the next.  So the taken cells of a bucket are a prefix of it,
   // and a position absent from a bucket whose last cell is free is absent
-  // from the table.  Probes read whole buckets (two 16-byte reads) and read
-  // the matched cell's index once, after their loop.
+  // from the table.  Probes read whole buckets (16-byte reads) and read the
+  // matched cell's index once, after their loop.
   int32_t* Hc = (int32_t*)(smem + L.off_hash);
   uint16_t* Hi = (uint16_t*)(smem + L.off_hidx);
   int32_t* Hn = (int32_t*)(smem + L.off_hcnt);
@@ -428,8 +428,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // may be wrong, and the index check below keeps every access in range.
   int hidx[SPT];  // top-k index of the pending entry this slot's token matches, or -1
   {
+    constexpr int BV = kBucketCells / 4;  // 16-byte reads per bucket
+    static_assert(kBucketCells == 4 || kBucketCells == 8, "bucket reads");
     uint32_t g[SPT];
-    i32x4 va[SPT], vb[SPT];
+    i32x4 v[SPT][BV];
     int hcell[SPT];  // table cell holding this slot's token, or -1
     unsigned live = 0;
 #pragma unroll
@@ -437,8 +439,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       const int tok = sr[j];
       if ((s0 + j < S) && tok >= 0 && (int64_t)tok < n) live |= 1u << j;
       g[j] = hash_pos(tok, bshift);  // in range for any token
-      va[j] = ((const i32x4*)Hc)[2 * g[j]];
-      vb[j] = ((const i32x4*)Hc)[2 * g[j] + 1];
+#pragma unroll
+      for (int e = 0; e < BV; ++e) v[j][e] = ((const i32x4*)Hc)[BV * g[j] + e];
       hcell[j] = -1;
     }
     while (true) {
@@ -446,14 +448,18 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
 #pragma unroll
       for (int j = 0; j < SPT; ++j) {
         const int tok = sr[j];
-        const bool m0 = va[j].x == tok, m1 = va[j].y == tok, m2 = va[j].z == tok, m3 = va[j].w == tok;
-        const bool m4 = vb[j].x == tok, m5 = vb[j].y == tok, m6 = vb[j].z == tok, m7 = vb[j].w == tok;
-        const bool any = m0 | m1 | m2 | m3 | m4 | m5 | m6 | m7;
-        const int q = ((m1 | m3 | m5 | m7) ? 1 : 0) | ((m2 | m3 | m6 | m7) ? 2 : 0) |
-                      ((m4 | m5 | m6 | m7) ? 4 : 0);
+        const bool m0 = v[j][0].x == tok, m1 = v[j][0].y == tok, m2 = v[j][0].z == tok, m3 = v[j][0].w == tok;
+        bool any = m0 | m1 | m2 | m3;
+        int q = ((m1 | m3) ? 1 : 0) | ((m2 | m3) ? 2 : 0);
+        if constexpr (BV == 2) {
+          const bool m4 = v[j][1].x == tok, m5 = v[j][1].y == tok, m6 = v[j][1].z == tok, m7 = v[j][1].w == tok;
+          any = any | m4 | m5 | m6 | m7;
+          q = ((m1 | m3 | m5 | m7) ? 1 : 0) | ((m2 | m3 | m6 | m7) ? 2 : 0) | ((m4 | m5 | m6 | m7) ? 4 : 0);
+        }
         const bool lj = (live >> j) & 1u;
         hcell[j] = (lj && any) ? (int)(kBucketCells * g[j]) + q : hcell[j];
-        next |= (lj && !any && vb[j].w != -1) ? 1u << j : 0u;  // full bucket, no match: the next one
+        // a full bucket without a match: the next one
+        next |= (lj && !any && v[j][BV - 1].w != -1) ? 1u << j : 0u;
       }
       if (next == 0) break;
       live = next;
@@ -461,8 +467,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       for (int j = 0; j < SPT; ++j) {
         const bool nj = (next >> j) & 1u;
         g[j] = nj ? (g[j] + 1) & (NBK - 1) : g[j];
-        va[j] = ((const i32x4*)Hc)[2 * g[j]];
-        vb[j] = ((const i32x4*)Hc)[2 * g[j] + 1];
+#pragma unroll
+        for (int e = 0; e < BV; ++e) v[j][e] = ((const i32x4*)Hc)[BV * g[j] + e];
       }
     }
 #pragma unroll
