@@ -72,12 +72,13 @@ typedef struct {
                              1..16384                                           */
   int32_t max_top_k;      /* largest top_k of any call, 1..S and <= 4096.  The
                              resolver keeps one request's table in 160 KB of
-                             LDS, about max(6*pow2(4k) + 4k, 8*pow2(S)) + 16k
-                             bytes (the table drops to 2 cells per entry
-                             when 4 do not fit); init returns EUNSUPPORTED
-                             for a pair that does not fit.  k=2048 needs
-                             91 KB at S=4096 and 99 KB at S=6144; S <= 8192
-                             allows k up to 4096, S=16384 up to 2004.           */
+                             LDS, about max(7*pow2(8k) + 4k, 8*pow2(S)) + 16k
+                             bytes (the table drops to 4, then 2, cells per
+                             entry when 8 do not fit); init returns
+                             EUNSUPPORTED for a pair that does not fit.
+                             k=2048 needs 153 KB at S=4096 and at S=6144;
+                             S <= 8192 allows k up to 4096, S=16384 up to
+                             2004.                                              */
   int32_t max_batch;      /* largest batch of any call (sizes the miss plan),
                              1..65535                                           */
   int32_t row_bytes;      /* bytes per KV row, a multiple of 16 (656 for the

@@ -92,7 +92,8 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
 /*
  * Hit detection alone, both ways round, for a measured comparison: one
  * 1024-thread workgroup per batch row on `stream`, the same single-cell
- * linear probing and 4 table cells per inserted item either way.
+ * linear probing and 4 table cells per inserted item either way (simpler
+ * than the resolver's own bucketed table).
  * out[b][i] (int32 [batch][top_k]) = the lowest slot s of request
  * req_idx[b] (clamped to [0, max_requests)) with slot_tokens[r][s] equal to
  * entry i's position, or -1 (also for positions outside
