@@ -743,15 +743,26 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       const uint32_t binc = wave_inclusive_sum(bcnt);
       const int tot = __builtin_amdgcn_readlane((int)binc, 63);
       const int cexcl = (int)(binc - bcnt);  // lane d: candidates of keys below base + d
+      // Every slot's three LDS reads are issued before any is used (a slot
+      // outside the window reads key 0's and ignores it), four slots at a time.
+      constexpr int RC = SPT < 4 ? SPT : 4;
 #pragma unroll
-      for (int j = 0; j < SPT; ++j) {
-        const int d = (inwin & (1u << j)) ? dd[j] : 0;
-        const int below = __shfl(cexcl, d, kWave);
-        if (inwin & (1u << j)) {
-          const uint64_t word = bm[wrd * BST + d];
-          const int rank = below + (int)wpre[wrd * BST + d] +
-                           __popcll(word & ((1ull << (bit0 + j)) - 1ull));
-          if (rank < need) vr[j] = vbase + rank;
+      for (int j0 = 0; j0 < SPT; j0 += RC) {
+        int below[RC], wp[RC];
+        uint64_t word[RC];
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+          const int j = j0 + c;
+          const int d = (inwin & (1u << j)) ? dd[j] : 0;
+          below[c] = __shfl(cexcl, d, kWave);
+          word[c] = bm[wrd * BST + d];
+          wp[c] = (int)wpre[wrd * BST + d];
+        }
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+          const int j = j0 + c;
+          const int rank = below[c] + wp[c] + __popcll(word[c] & ((1ull << (bit0 + j)) - 1ull));
+          if ((inwin & (1u << j)) && rank < need) vr[j] = vbase + rank;
         }
       }
       cand &= ~inwin;
