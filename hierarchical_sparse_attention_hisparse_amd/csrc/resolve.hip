@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   int32_t* m_h = (int32_t*)(smem + L.off_mhost);
   uint64_t* s_sort = (uint64_t*)(smem + L.off_sort);
   const int HS = L.hash_size;
-  const int NBK = HS / kBucketCells;        // buckets (a power of two >= 8)
+  const int NBK = HS / kBucketCells;        // buckets (a power of two >= 16)
   const int bshift = 32 - ilog2(NBK);
 
   for (int x = tid; x < HS / 4; x += kResolveThreads) ((i32x4*)Hc)[x] = i32x4{-1, -1, -1, -1};
