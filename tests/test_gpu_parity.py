@@ -82,6 +82,42 @@ def test_top_k_equals_slots(mode):
     run_parity(w, log=_log("k=S"), mode=mode)
 
 
+def _table_bucket(t, nbk):
+    """The bucket a position hashes to in the resolver's table of nbk buckets
+    (Knuth's multiplicative hash, top log2(nbk) bits of the 32-bit product)."""
+    t = np.asarray(t, dtype=np.uint64)
+    return ((t * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)) >> np.uint64(32 - int(np.log2(nbk)))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_table_bucket_overflow_and_wraparound(mode):
+    """Every step each row's top-k starts with 60 positions drawn from the
+    ones that hash into the table's last two buckets, so inserts overflow
+    across a chain of buckets that wraps past the table's end, and probes
+    walk it.  The draws overlap from step to step, so slots hold some of
+    those positions as hits and others that are not pending (probes that
+    must end absent).  The table shape assumed is the kernel's at S=512,
+    k=256: 8 cells per entry in buckets of 4, 512 buckets.  Were it another,
+    the comparison would still be bit-exact, only the stress weaker."""
+    print("[collide %s] S=512 k=256" % mode, flush=True)
+    S, k, n = 512, 256, 60000
+    w = synth("collide", 71, R=8, S=S, k=k, steps=5, n0=[n] * 8, keep=128)
+    nbk = 8 * k // 4
+    pos = np.arange(n, dtype=np.int64)
+    bk = _table_bucket(pos, nbk)
+    pool = np.concatenate([pos[bk == nbk - 1], pos[bk == nbk - 2]])
+    assert len(pool) >= 200
+    rng = np.random.default_rng(17)
+    for step in range(w.steps):
+        for b in range(w.B):
+            hot = rng.choice(pool, size=60, replace=False).tolist()
+            taken = set(hot)
+            rest = [int(x) for x in w.top_k[step, b] if x >= 0 and int(x) not in taken]
+            w.top_k[step, b] = np.array(hot + rest[:k - 60], dtype=np.int32)
+    stats = run_parity(w, log=_log("collide"), mode=mode)
+    assert stats[0] > 0 and stats[1] > 0
+
+
 def test_zero_top_k_and_empty_batch():
     w = synth("k0", 25, R=2, S=64, k=8, steps=1, n0=[500, 100])
     bufs = make_host_pools(w)
