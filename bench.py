@@ -514,9 +514,12 @@ def plan_phases(w, g, hs, torch, stream, args):
         torch.cuda.synchronize()
         floors[name] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
     res["floors_us"] = floors
-    # hit detection alone, both ways round (same probing, same launch shape)
+    # hit detection alone, both ways round, single-cell and bucketed tables
+    # (same launch shape)
     hit, outs = {}, []
-    for mode, name in ((0, "positions_table_probed_by_slots"), (1, "slot_map_probed_by_entries")):
+    for mode, name in ((0, "positions_table_probed_by_slots"), (1, "slot_map_probed_by_entries"),
+                       (2, "bucketed_positions_table_probed_by_slots"),
+                       (3, "bucketed_slot_map_probed_by_entries")):
         o = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
         fn = lambda n, mode=mode, o=o: hs.hisparse_diag_hit_detection(
             stream, mode, w.B, w.k, w.S, w.R, w.max_seq_len, g["req"], g["topk"][i_last],
@@ -529,7 +532,7 @@ def plan_phases(w, g, hs, torch, stream, args):
         torch.cuda.synchronize()
         hit[name] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
         outs.append(o)
-    hit["same_result"] = bool(torch.equal(outs[0], outs[1]))
+    hit["same_result"] = all(bool(torch.equal(outs[0], o)) for o in outs[1:])
     res["hit_detection_us"] = hit
     # splitting a request over G workgroups: a last-arriver exchange per row
     # (partials, agent-scope fence, arrival counter), G x batch workgroups

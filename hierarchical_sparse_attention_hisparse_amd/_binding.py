@@ -495,7 +495,8 @@ def hisparse_diag_exchange(stream, batch, groups, scratch, launches=1):
 def hisparse_diag_hit_detection(stream, mode, batch, top_k, slots, max_requests, max_seq_len,
                                 req_idx, top_k_tokens, seq_lens, slot_tokens, out, launches=1):
     """Hit detection alone (mode 0: positions table probed by the slots; mode 1:
-    slot -> token map probed by the entries); ``out`` int32 [batch, top_k]."""
+    slot -> token map probed by the entries; modes 2 and 3: the same with
+    bucketed tables); ``out`` int32 [batch, top_k]."""
     import torch
     rp = _dev(req_idx, torch.int32, (batch,), "req_idx")
     tp = _dev(top_k_tokens, torch.int32, (batch, top_k), "top_k_tokens")

@@ -93,13 +93,19 @@ __global__ __launch_bounds__(kFloorThreads) void floor_chain_kernel(FloorParams 
 }
 
 // Hit detection alone, both ways round, one 1024-thread workgroup per batch
-// row, with the same single-cell linear probing and 4 table cells per
-// inserted item in both: out[b][i] = the lowest slot of the request holding
-// entry i's position, or -1.
+// row: out[b][i] = the lowest slot of the request holding entry i's
+// position, or -1.
 //   MODE 0: the entries' positions go into the table (top-k index per cell)
 //           and every slot probes it with its token (the library's way);
 //   MODE 1: the slots' tokens go into the table (lowest slot per cell) and
 //           every entry probes it with its position (a slot -> token map).
+// Modes 0 and 1 use single-cell linear probing with 4 cells per inserted
+// item.  Modes 2 and 3 are the same two directions with the resolver's kind
+// of table: buckets of 4 cells handed out in order by a fill count per
+// bucket (one atomic add per insert, the next bucket past a full one) and
+// read 16 bytes at a time; mode 2 has 8 cells per entry, as the resolver
+// does (4 at k = 4096), mode 3 4 cells per slot (8 would take 256 KB of
+// LDS at S = 4096).
 constexpr int kHitMaxK = 4096, kHitMaxS = 4096;
 
 __device__ inline uint32_t hit_hash(int t, int shift) { return ((uint32_t)t * 2654435761u) >> shift; }
@@ -112,15 +118,19 @@ struct HitParams {
   const int32_t* seq;
   const int32_t* st;
   int32_t* out;
-  int32_t cells, shift;  // table cells (power of two) and hash shift
+  int32_t cells, shift;  // table cells (power of two) and hash shift (modes 2, 3: of the buckets)
 };
+
+typedef int hit_i32x4 __attribute__((ext_vector_type(4)));
 
 template <int MODE>
 __global__ __launch_bounds__(kFloorThreads) void hit_detect_kernel(HitParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   int32_t* key = (int32_t*)smem;           // [cells]: position / token, -1 = free
   int32_t* val = key + p.cells;            // [cells]: MODE 0 top-k index, MODE 1 lowest slot
-  int32_t* ehit = val + p.cells;           // MODE 0: [k] lowest hit slot per entry
+  int32_t* ehit = val + p.cells;           // MODES 0, 2: [k] lowest hit slot per entry
+  int32_t* cnt = ehit + (MODE == 2 ? p.k : 0);  // MODES 2, 3: [cells / 4] fill count per bucket
+  const int nbk = p.cells / 4;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int r = clamp_req(p.req[b], p.R);
   const int64_t n = p.seq[b] < p.max_seq_len ? (int64_t)p.seq[b] : p.max_seq_len;
@@ -131,10 +141,71 @@ __global__ __launch_bounds__(kFloorThreads) void hit_detect_kernel(HitParams p) 
     key[x] = -1;
     val[x] = INT_MAX;
   }
-  if (MODE == 0)
+  if (MODE == 0 || MODE == 2)
     for (int i = tid; i < p.k; i += kFloorThreads) ehit[i] = INT_MAX;
+  if (MODE >= 2)
+    for (int x = tid; x < nbk; x += kFloorThreads) cnt[x] = 0;
   __syncthreads();
-  if (MODE == 0) {
+  // A bucketed insert: the cell the bucket's fill count names, past full
+  // buckets (the table has at least twice as many cells as items).
+  auto bucket_insert = [&](int t, int v) {
+    uint32_t bk = hit_hash(t, p.shift);
+    int c = atomicAdd(&cnt[bk], 1);
+    while (c >= 4) {
+      bk = (bk + 1) & (uint32_t)(nbk - 1);
+      c = atomicAdd(&cnt[bk], 1);
+    }
+    key[4 * bk + c] = t;
+    val[4 * bk + c] = v;
+  };
+  if (MODE == 2) {
+    for (int i = tid; i < p.k; i += kFloorThreads) {
+      const int t = tk[i];
+      if (t < 0 || (int64_t)t >= n) continue;
+      bucket_insert(t, i);
+    }
+    __syncthreads();
+    for (int s = tid; s < p.S; s += kFloorThreads) {
+      const int tok = st[s];
+      if (tok < 0 || (int64_t)tok >= n) continue;
+      for (uint32_t bk = hit_hash(tok, p.shift);; bk = (bk + 1) & (uint32_t)(nbk - 1)) {
+        const hit_i32x4 v = ((const hit_i32x4*)key)[bk];  // positions are distinct: one match at most
+        const int q = v.x == tok ? 0 : v.y == tok ? 1 : v.z == tok ? 2 : v.w == tok ? 3 : -1;
+        if (q >= 0) {
+          atomicMin(&ehit[val[4 * bk + q]], s);
+          break;
+        }
+        if (v.w == -1) break;  // a bucket with room ends the chain
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < p.k; i += kFloorThreads)
+      p.out[(int64_t)b * p.k + i] = ehit[i] == INT_MAX ? -1 : ehit[i];
+  } else if (MODE == 3) {
+    for (int s = tid; s < p.S; s += kFloorThreads) {
+      const int tok = st[s];
+      if (tok < 0 || (int64_t)tok >= n) continue;
+      bucket_insert(tok, s);
+    }
+    __syncthreads();
+    for (int i = tid; i < p.k; i += kFloorThreads) {
+      const int t = tk[i];
+      int res = INT_MAX;
+      if (t >= 0 && (int64_t)t < n) {
+        // A token held by several slots sits in several cells, all on its
+        // chain up to the first bucket with room: the lowest slot of them.
+        for (uint32_t bk = hit_hash(t, p.shift);; bk = (bk + 1) & (uint32_t)(nbk - 1)) {
+          const hit_i32x4 v = ((const hit_i32x4*)key)[bk];
+          if (v.x == t) res = min(res, val[4 * bk]);
+          if (v.y == t) res = min(res, val[4 * bk + 1]);
+          if (v.z == t) res = min(res, val[4 * bk + 2]);
+          if (v.w == t) res = min(res, val[4 * bk + 3]);
+          if (v.w == -1) break;
+        }
+      }
+      p.out[(int64_t)b * p.k + i] = res == INT_MAX ? -1 : res;
+    }
+  } else if (MODE == 0) {
     for (int i = tid; i < p.k; i += kFloorThreads) {
       const int t = tk[i];
       if (t < 0 || (int64_t)t >= n) continue;
@@ -296,7 +367,7 @@ int hisparse_diag_hit_detection(void* stream, int32_t mode, int32_t batch, int32
                                 int32_t max_requests, int64_t max_seq_len, const int32_t* req_idx,
                                 const int32_t* top_k_tokens, const int32_t* seq_lens,
                                 const int32_t* slot_tokens, int32_t* out, int32_t launches) {
-  if (mode < 0 || mode > 1) return report_error(HISPARSE_EINVAL, "mode %d not in [0, 1]", mode);
+  if (mode < 0 || mode > 3) return report_error(HISPARSE_EINVAL, "mode %d not in [0, 3]", mode);
   if (batch < 1 || batch > 65535) return report_error(HISPARSE_EINVAL, "batch %d not in [1, 65535]", batch);
   if (top_k < 1 || top_k > kHitMaxK)
     return report_error(HISPARSE_EINVAL, "top_k %d not in [1, %d]", top_k, kHitMaxK);
@@ -309,23 +380,35 @@ int hisparse_diag_hit_detection(void* stream, int32_t mode, int32_t batch, int32
     return report_error(HISPARSE_EINVAL, "a device array is NULL");
   if (launches < 1 || launches > (1 << 20))
     return report_error(HISPARSE_EINVAL, "launches %d not in [1, 1048576]", launches);
-  const int items = mode == 0 ? top_k : slots;
+  const int items = (mode == 0 || mode == 2) ? top_k : slots;
+  const int per = mode == 2 ? 8 : 4;  // cells per inserted item
   int cells = 64;
-  while (cells < 4 * items) cells <<= 1;
+  while (cells < per * items) cells <<= 1;
+  auto lds_of = [&](int c) {
+    return (size_t)2 * c * sizeof(int32_t) + ((mode == 0 || mode == 2) ? (size_t)top_k * sizeof(int32_t) : 0) +
+           (mode >= 2 ? (size_t)(c / 4) * sizeof(int32_t) : 0);
+  };
+  while (lds_of(cells) > kLdsBudget && cells / 2 >= 2 * items) cells >>= 1;  // k = 4096, mode 2: 4 per entry
+  const size_t lds = lds_of(cells);
   int lg = 0;
-  while ((1 << lg) < cells) ++lg;
+  while ((1 << lg) < (mode >= 2 ? cells / 4 : cells)) ++lg;
   HitParams p{top_k, slots, max_requests, max_seq_len, req_idx, top_k_tokens, seq_lens, slot_tokens,
               out, cells, 32 - lg};
-  const size_t lds = (size_t)2 * cells * sizeof(int32_t) + (mode == 0 ? (size_t)top_k * sizeof(int32_t) : 0);
-  const void* fn = mode == 0 ? (const void*)hit_detect_kernel<0> : (const void*)hit_detect_kernel<1>;
+  const void* fns[4] = {(const void*)hit_detect_kernel<0>, (const void*)hit_detect_kernel<1>,
+                        (const void*)hit_detect_kernel<2>, (const void*)hit_detect_kernel<3>};
+  const void* fn = fns[mode];
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return report_error(HISPARSE_EHIP, "hit detection set-up: %s", hipGetErrorString(e));
   const hipStream_t s = (hipStream_t)stream;
   for (int n = 0; n < launches; ++n) {
     if (mode == 0)
       hipLaunchKernelGGL(hit_detect_kernel<0>, dim3(batch), dim3(kFloorThreads), lds, s, p);
-    else
+    else if (mode == 1)
       hipLaunchKernelGGL(hit_detect_kernel<1>, dim3(batch), dim3(kFloorThreads), lds, s, p);
+    else if (mode == 2)
+      hipLaunchKernelGGL(hit_detect_kernel<2>, dim3(batch), dim3(kFloorThreads), lds, s, p);
+    else
+      hipLaunchKernelGGL(hit_detect_kernel<3>, dim3(batch), dim3(kFloorThreads), lds, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return report_error(HISPARSE_EHIP, "hit detection launch: %s", hipGetErrorString(e));
   }

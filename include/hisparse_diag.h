@@ -91,9 +91,7 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
 
 /*
  * Hit detection alone, both ways round, for a measured comparison: one
- * 1024-thread workgroup per batch row on `stream`, the same single-cell
- * linear probing and 4 table cells per inserted item either way (simpler
- * than the resolver's own bucketed table).
+ * 1024-thread workgroup per batch row on `stream`.
  * out[b][i] (int32 [batch][top_k]) = the lowest slot s of request
  * req_idx[b] (clamped to [0, max_requests)) with slot_tokens[r][s] equal to
  * entry i's position, or -1 (also for positions outside
@@ -101,7 +99,12 @@ int hisparse_diag_floor(void* stream, int32_t kind, int32_t batch, int32_t top_k
  *   0 the entries' positions go into an LDS table and every slot probes it
  *     with its token (the plan kernel's direction);
  *   1 the slots' tokens go into an LDS table (a slot -> token map, lowest
- *     slot per token) and every entry probes it with its position.
+ *     slot per token) and every entry probes it with its position;
+ *   2, 3 the same two directions with the plan kernel's kind of table:
+ *     buckets of 4 cells filled in order through a fill count per bucket
+ *     and read 16 bytes at a time; 8 cells per entry for 2 (4 at
+ *     top_k = 4096), 4 per slot for 3.
+ * Modes 0 and 1 use single-cell linear probing, 4 cells per inserted item.
  * Positions within a row must be distinct, as for hisparse_resolve.
  * Launched `launches` times back to back.  Returns HISPARSE_EINVAL for a bad
  * mode, a NULL array, 1 <= batch <= 65535, 1 <= top_k <= 4096,

@@ -147,32 +147,34 @@ def main():
     say("last-arriver exchange sums every partial and resets its counters")
 
     # 5. hit detection both ways round: the lowest slot holding each entry's
-    #    position (brute force), identical for both modes
-    B, k, S, R, n = 6, 900, 700, 4, 5000
-    req = torch.tensor([0, 3, 1, -2, 7, 2], dtype=torch.int32)
-    seq = torch.tensor([5000, 4000, 3000, 5000, 100, 2500], dtype=torch.int32)
-    topk = torch.stack([torch.randperm(n + 40, generator=g)[:k] - 20 for _ in range(B)]).to(torch.int32)
-    st = torch.randint(-3, n, (R, S), generator=g, dtype=torch.int32)
-    st[:, 1::7] = st[:, 0::7][:, :st[:, 1::7].shape[1]]   # repeated tokens: the lowest slot wins
-    rc = np.clip(req.numpy(), 0, R - 1)
-    want = np.full((B, k), -1, dtype=np.int64)
-    stn = st.numpy()
-    for b in range(B):
-        lowest = {}
-        for s in range(S - 1, -1, -1):
-            lowest[int(stn[rc[b], s])] = s
-        for i in range(k):
-            t = int(topk[b, i])
-            if 0 <= t < min(int(seq[b]), n) and t in lowest:
-                want[b, i] = lowest[t]
-    for mode in (0, 1):
-        out = torch.full((B, k), -7, dtype=torch.int32, device=dev)
-        hs.hisparse_diag_hit_detection(None, mode, B, k, S, R, n, d(req), d(topk), d(seq), d(st), out,
-                                       launches=2)
-        torch.cuda.synchronize()
-        assert np.array_equal(out.cpu().numpy().astype(np.int64), want), ("hit detection", mode)
-    assert (want >= 0).sum() > 100
-    say("hit detection both ways round gives the lowest slot of every entry's position")
+    #    position (brute force), identical for all four modes; at the largest
+    #    shape too (k = S = 4096, where mode 2's table drops to 4 cells per
+    #    entry to fit the LDS)
+    for B, k, S, R, n in ((6, 900, 700, 4, 5000), (2, 4096, 4096, 2, 20000)):
+        req = torch.tensor([0, 3, 1, -2, 7, 2][:B], dtype=torch.int32)
+        seq = torch.tensor([5000, 4000, 3000, 5000, 100, 2500][:B], dtype=torch.int32) * (n // 5000)
+        topk = torch.stack([torch.randperm(n + 40, generator=g)[:k] - 20 for _ in range(B)]).to(torch.int32)
+        st = torch.randint(-3, n, (R, S), generator=g, dtype=torch.int32)
+        st[:, 1::7] = st[:, 0::7][:, :st[:, 1::7].shape[1]]   # repeated tokens: the lowest slot wins
+        rc = np.clip(req.numpy(), 0, R - 1)
+        want = np.full((B, k), -1, dtype=np.int64)
+        stn = st.numpy()
+        for b in range(B):
+            lowest = {}
+            for s in range(S - 1, -1, -1):
+                lowest[int(stn[rc[b], s])] = s
+            for i in range(k):
+                t = int(topk[b, i])
+                if 0 <= t < min(int(seq[b]), n) and t in lowest:
+                    want[b, i] = lowest[t]
+        for mode in (0, 1, 2, 3):
+            out = torch.full((B, k), -7, dtype=torch.int32, device=dev)
+            hs.hisparse_diag_hit_detection(None, mode, B, k, S, R, n, d(req), d(topk), d(seq), d(st), out,
+                                           launches=2)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().astype(np.int64), want), ("hit detection", mode, k, S)
+        assert (want >= 0).sum() > 100
+    say("hit detection both ways round, single-cell and bucketed, gives the lowest slot of every entry's position")
     print("DIAG OK", flush=True)
 
 

@@ -192,7 +192,7 @@ def test_diagnostic_header_is_plain_c_and_links_from_c(tmp_path):
         "  int a = hisparse_diag_phase_read(w, 1);\n"
         "  int b = hisparse_diag_floor(NULL, 9, 1, 1, 1, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, 1);\n"
         "  int c = hisparse_diag_exchange(NULL, 1, 0, NULL, 1);\n"
-        "  int d = hisparse_diag_hit_detection(NULL, 2, 1, 1, 1, 1, 1, NULL, NULL, NULL, NULL, NULL, 1);\n"
+        "  int d = hisparse_diag_hit_detection(NULL, 9, 1, 1, 1, 1, 1, NULL, NULL, NULL, NULL, NULL, 1);\n"
         '  printf("%d %d %d %d %d %s\\n", a, b, c, d, HISPARSE_TRACE_WORDS, hisparse_last_error());\n'
         "  return a == HISPARSE_EINVAL && b == HISPARSE_EINVAL && c == HISPARSE_EINVAL &&\n"
         "         d == HISPARSE_EINVAL ? 0 : 1;\n"
