@@ -38,6 +38,7 @@ struct ResolveParams {
   const uint4* zero_row;                   // device, `units` zero 16-byte units
   int32_t units;                           // row_bytes / 16
   int32_t copy_layers;                     // 0 = plan only, else <= kMaxFusedLayers
+  int32_t P_shift;  // log2(P) when P is a power of two, else -1 (set by launch_resolve)
 };
 
 struct CopyParams {

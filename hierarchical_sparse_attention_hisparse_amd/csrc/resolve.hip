@@ -224,7 +224,9 @@ static_assert(kScrBtot + kMaxRankBins <= kScrInts, "scratch layout");
 
 // COPY: the workgroup also copies its misses into p.copy_layers layers.
 // VEC: each thread's slot-state run is loaded as vectors.
-template <int SPT, int KPT, bool COPY, bool VEC>
+// PAGED: a block table maps resident pages (p.bt not null).  A separate
+// instance: the rows without one then carry no page code at all.
+template <int SPT, int KPT, bool COPY, bool VEC, bool PAGED>
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -332,13 +334,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   // Block-table entries of this thread's positions, at in-range indices,
   // issued with the slot-state loads so that both round trips overlap.
   int pgs[KPT];
-  if (p.bt != nullptr) {
+  if constexpr (PAGED) {
     const int32_t* btr = p.bt + (int64_t)r * p.max_pages;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int t = tr[j];
       const bool v = t >= 0 && (int64_t)t < n;
-      pgs[j] = btr[v ? t / p.P : 0];
+      // (a power-of-two page size divides by a shift: a uniform branch)
+      pgs[j] = btr[v ? (p.P_shift >= 0 ? t >> p.P_shift : t / p.P) : 0];
     }
   }
 
@@ -390,10 +393,11 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
       outb[i] = -1;
       continue;
     }
-    if (p.bt != nullptr) {
+    if constexpr (PAGED) {
       const int pg = pgs[j];
       if (pg >= 0 && (int64_t)pg < p.resident_pages) {
-        outb[i] = (int)((int64_t)p.R * S + (int64_t)pg * p.P + t % p.P);
+        const int off = p.P_shift >= 0 ? (t & (p.P - 1)) : t % p.P;
+        outb[i] = (int)((int64_t)p.R * S + (int64_t)pg * p.P + off);
         ++n_res;
         continue;
       }
@@ -959,16 +963,22 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveParams 
   PHASE_POINT(7);
 }
 
-template <int SPT, int KPT>
-hipError_t launch_t(const ResolveParams& p, int batch, size_t lds, hipStream_t stream) {
+template <int SPT, int KPT, bool PAGED>
+void launch_p(const ResolveParams& p, int batch, size_t lds, hipStream_t stream) {
   const dim3 g(batch), t(kResolveThreads);
   if (p.copy_layers > 0) {
-    if (p.vec_state) hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true, true>), g, t, lds, stream, p);
-    else hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true, false>), g, t, lds, stream, p);
+    if (p.vec_state) hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true, true, PAGED>), g, t, lds, stream, p);
+    else hipLaunchKernelGGL((resolve_kernel<SPT, KPT, true, false, PAGED>), g, t, lds, stream, p);
   } else {
-    if (p.vec_state) hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false, true>), g, t, lds, stream, p);
-    else hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false, false>), g, t, lds, stream, p);
+    if (p.vec_state) hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false, true, PAGED>), g, t, lds, stream, p);
+    else hipLaunchKernelGGL((resolve_kernel<SPT, KPT, false, false, PAGED>), g, t, lds, stream, p);
   }
+}
+
+template <int SPT, int KPT>
+hipError_t launch_t(const ResolveParams& p, int batch, size_t lds, hipStream_t stream) {
+  if (p.bt != nullptr) launch_p<SPT, KPT, true>(p, batch, lds, stream);
+  else launch_p<SPT, KPT, false>(p, batch, lds, stream);
   return hipGetLastError();
 }
 
@@ -984,10 +994,14 @@ hipError_t launch_k(const ResolveParams& p, int batch, size_t lds, hipStream_t s
 
 template <int SPT, int KPT>
 hipError_t set_attr() {
-  const void* fns[4] = {(const void*)resolve_kernel<SPT, KPT, false, false>,
-                        (const void*)resolve_kernel<SPT, KPT, false, true>,
-                        (const void*)resolve_kernel<SPT, KPT, true, false>,
-                        (const void*)resolve_kernel<SPT, KPT, true, true>};
+  const void* fns[8] = {(const void*)resolve_kernel<SPT, KPT, false, false, false>,
+                        (const void*)resolve_kernel<SPT, KPT, false, true, false>,
+                        (const void*)resolve_kernel<SPT, KPT, true, false, false>,
+                        (const void*)resolve_kernel<SPT, KPT, true, true, false>,
+                        (const void*)resolve_kernel<SPT, KPT, false, false, true>,
+                        (const void*)resolve_kernel<SPT, KPT, false, true, true>,
+                        (const void*)resolve_kernel<SPT, KPT, true, false, true>,
+                        (const void*)resolve_kernel<SPT, KPT, true, true, true>};
   for (const void* f : fns) {
     const hipError_t e =
         hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
@@ -1010,6 +1024,7 @@ hipError_t set_attr_k() {
 hipError_t launch_resolve(ResolveParams p, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   p.lds = resolve_lds_layout(p.S, p.k);
+  p.P_shift = (p.P > 0 && (p.P & (p.P - 1)) == 0) ? ilog2(p.P) : -1;
   const size_t lds = p.lds.total;
   const int spt = resolve_slots_per_thread(p.S);
   const int kpt = resolve_entries_per_thread(p.k);
