@@ -938,7 +938,7 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": "resolve_kernel<4,2,true>: plan + fused miss copy, one launch per step",
+            "kernel": "resolve_kernel<4, 2, true, true, false>: plan + fused miss copy, one launch per step",
             "bound": "host_link",
             "achieved": step_gbs,
             "peak": HOST_LINK_PEAK_GBS,
@@ -954,7 +954,7 @@ def main():
             "avg_launch_ms": step_ms,
         },
         "roofline_plan": {
-            "kernel": "resolve_kernel<4,2,false>: plan only (split entry point)",
+            "kernel": "resolve_kernel<4, 2, false, true, false>: plan only (split entry point)",
             "bound": "hbm",
             "achieved": plan_gbs,
             "peak": HBM_PEAK_GBS,
