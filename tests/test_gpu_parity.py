@@ -375,3 +375,36 @@ def test_duplicate_positions_are_safe(mode):
         assert stats[0] > 0 and stats[1] > 0 and stats[4] == 0
     finally:
         pair.close()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("row_bytes", [16, 1040, 2064])
+def test_row_widths(mode, row_bytes):
+    """Rows of any multiple of 16 bytes: one 16-byte unit, and rows of 65
+    and 129 units, more than one unit per lane (the fused instance then
+    skips its early loads of the first layer's rows and every lane copies
+    several units).  Two layers, fast-path and LRU rows and a padding row;
+    every step's named rows and the whole pools are compared."""
+    print("[row widths %s %d]" % (mode, row_bytes), flush=True)
+    w = synth("rows%d" % row_bytes, 77 + row_bytes, R=12, S=256, k=96, steps=4,
+              n0=[300, 700, 1500, 90, 2000, 256, 1200, 5000, 640, 3000], L=2, grow=3,
+              keep=60, recent=16, recent_window=90, padding_rows=1)
+    w.row_bytes = row_bytes
+    stats = run_parity(w, mode=mode)
+    assert stats[1] > 0  # misses were copied
+
+
+def test_largest_batch():
+    """The largest batch a pool admits (65,535 rows, one workgroup each),
+    with 5 padding rows among them and one-unit rows to keep the pools small:
+    two steps through the single-call entry point, bit-exact."""
+    B, pad = 65535, 5
+    rng = np.random.default_rng(5)
+    n0 = [int(v) for v in rng.integers(1, 64, size=B - pad)]
+    print("[largest batch %d]" % B, flush=True)
+    w = synth("maxbatch", 90, R=B - pad, S=16, k=8, steps=2, n0=n0, grow=1, keep=5,
+              recent=1, recent_window=1, padding_rows=pad)
+    w.row_bytes = 16
+    assert w.B == 65535
+    stats = run_parity(w)
+    assert stats[1] > 0
