@@ -75,6 +75,20 @@ def test_resident_pages_small(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("P,tail", [(1, 256), (24, 240), (100, 300)])
+def test_resident_page_sizes(mode, P, tail):
+    """Single-token pages and page sizes that are not powers of two (the
+    block-table lookup then divides instead of shifting), on rows that grow
+    every step, with a padding row."""
+    print("[resident %s] P=%d tail=%d" % (mode, P, tail), flush=True)
+    w = synth("pages%d" % P, 31 + P, R=8, S=256, k=128, steps=5,
+              n0=[2048, 3000, 1000, 5000, 700, 4096, 2500, 6000], grow=7, keep=90,
+              P=P, resident_tail=tail, padding_rows=1)
+    stats = run_parity(w, mode=mode)
+    assert stats[2] > 0
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_top_k_equals_slots(mode):
     print("[k=S %s] S=k=2048" % mode, flush=True)
     w = synth("kS", 24, R=8, S=2048, k=2048, steps=4,
