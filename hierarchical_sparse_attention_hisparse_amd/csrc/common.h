@@ -135,12 +135,12 @@ inline int resolve_entries_per_thread(int k) {
   return next_pow2(v < 1 ? 1 : v);
 }
 constexpr int kMaxSlotsPerThread = 16;
+constexpr int kMaxEntriesPerThread = kMaxTopK / kResolveThreads;  // 4
 
 // Phase trace of the plan kernel (diagnostic build only, HISPARSE_PHASE_TRACE):
 // batch rows traced and points per wavefront (8 phase points, then one of
 // ranking information).
 constexpr int kTraceRows = 256;
 constexpr int kTracePoints = 9;
-constexpr int kMaxEntriesPerThread = 8;
 
 }  // namespace hisparse

@@ -987,8 +987,7 @@ hipError_t launch_k(const ResolveParams& p, int batch, size_t lds, hipStream_t s
   switch (kpt) {
     case 1: return launch_t<SPT, 1>(p, batch, lds, stream);
     case 2: return launch_t<SPT, 2>(p, batch, lds, stream);
-    case 4: return launch_t<SPT, 4>(p, batch, lds, stream);
-    default: return launch_t<SPT, 8>(p, batch, lds, stream);
+    default: return launch_t<SPT, 4>(p, batch, lds, stream);  // kMaxEntriesPerThread
   }
 }
 
@@ -1015,7 +1014,6 @@ hipError_t set_attr_k() {
   hipError_t e = set_attr<SPT, 1>();
   if (e == hipSuccess) e = set_attr<SPT, 2>();
   if (e == hipSuccess) e = set_attr<SPT, 4>();
-  if (e == hipSuccess) e = set_attr<SPT, 8>();
   return e;
 }
 
