@@ -25,11 +25,11 @@ def _normwise(got, ref):
     return np.where(den > 0, num / np.maximum(den, 1e-30), num)
 
 
-def _run_decode(dev_pool, locs_np, q, heads, max_top_k):
+def _run_decode(dev_pool, locs_np, q, heads, max_top_k, row_bytes=656):
     B, k = locs_np.shape
-    hb = hs.HostBuffer(656 * 16)
+    hb = hs.HostBuffer(row_bytes * 16)
     cfg = hs.PoolConfig(max_requests=1, slots=max(16, max_top_k), max_top_k=max(1, max_top_k),
-                        max_batch=B, max_seq_len=16, max_heads=heads)
+                        max_batch=B, max_seq_len=16, max_heads=heads, row_bytes=row_bytes)
     pool = hs.hisparse_init_pool(cfg, [hb], [16], [dev_pool], dev_pool.shape[0])
     try:
         locs = torch.from_numpy(locs_np).cuda()
@@ -69,6 +69,36 @@ def test_decode_small_vs_oracle(B, H, k):
     err = _normwise(got, ref)
     print("[decode] max normwise error %.3g" % err.max(), flush=True)
     assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("row_bytes", [672, 1024])
+def test_decode_padded_rows_vs_oracle(row_bytes):
+    """Rows stored at a stride above the 656-byte record (row_bytes a larger
+    multiple of 16).  The bytes past the record are all 0xFF, an e4m3 NaN
+    code, so reading any of them would turn outputs into NaN."""
+    print("[decode padded] row_bytes=%d" % row_bytes, flush=True)
+    B, H, k, rows = 3, 128, 200, 700
+    rec = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(rec, 41, gen_device="cuda")
+    dev = torch.full((rows, row_bytes), 0xFF, dtype=torch.uint8, device="cuda")
+    dev[:, :656] = rec
+    rng = np.random.default_rng(row_bytes)
+    locs = rng.integers(0, rows, size=(B, k)).astype(np.int32)
+    locs[0, ::5] = -1
+    q = make_queries(B, H, seed=9, device="cuda")
+    got = _run_decode(dev, locs, q, H, k, row_bytes=row_bytes)
+    assert np.isfinite(got).all()
+    ref = oracle_sparse_mla_decode(q.cpu().view(torch.int16).numpy().astype(np.uint16), locs,
+                                   dev.cpu().numpy(), float(np.float32(SCALE)), row_bytes=row_bytes)
+    err = _normwise(got, ref)
+    print("[decode padded] max normwise error %.3g" % err.max(), flush=True)
+    assert err.max() <= TOL
+    # the allocation-free entry point takes the stride from the pool tensor
+    out2 = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    hs.hisparse_sparse_mla_decode_noalloc(None, B, H, k, dev, q, torch.from_numpy(locs).cuda(),
+                                          SCALE, out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.float().cpu().numpy().astype(np.float64), got)
 
 
 @pytest.mark.parametrize("seed", range(12))
