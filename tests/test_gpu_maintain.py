@@ -14,24 +14,26 @@ pytestmark = pytest.mark.gpu
 RB = 656
 
 
-def _small_pool(R, S, L, dev_rows, host_rows, max_seq_len=64):
-    bufs = [hs.HostBuffer(host_rows * RB) for _ in range(L)]
+def _small_pool(R, S, L, dev_rows, host_rows, max_seq_len=64, rb=RB):
+    bufs = [hs.HostBuffer(host_rows * rb) for _ in range(L)]
     for l, hb in enumerate(bufs):
-        hb.numpy((host_rows, RB))[:] = 0x5A + l
-    devs = [torch.randint(0, 256, (dev_rows, RB), dtype=torch.uint8, device="cuda",
+        hb.numpy((host_rows, rb))[:] = 0x5A + l
+    devs = [torch.randint(0, 256, (dev_rows, rb), dtype=torch.uint8, device="cuda",
                           generator=torch.Generator(device="cuda").manual_seed(7 + l))
             for l in range(L)]
-    cfg = hs.PoolConfig(max_requests=R, slots=S, max_top_k=min(S, 64), max_batch=8, row_bytes=RB,
+    cfg = hs.PoolConfig(max_requests=R, slots=S, max_top_k=min(S, 64), max_batch=8, row_bytes=rb,
                         num_layers=L, max_seq_len=max_seq_len)
     pool = hs.hisparse_init_pool(cfg, bufs, [host_rows] * L, devs, dev_rows)
     return pool, bufs, devs
 
 
-@pytest.mark.parametrize("count", [1, 37, 5000])
-def test_mirror_rows_vs_oracle(count):
-    print("[mirror] count=%d" % count, flush=True)
+@pytest.mark.parametrize("count,rb", [(1, RB), (37, RB), (5000, RB), (37, 16), (600, 2064)])
+def test_mirror_rows_vs_oracle(count, rb):
+    """Rows of 656 bytes, of one 16-byte unit, and of 129 units (more than one
+    per lane)."""
+    print("[mirror] count=%d row_bytes=%d" % (count, rb), flush=True)
     L, dev_rows, host_rows = 2, 6000, 9000
-    pool, bufs, devs = _small_pool(R=4, S=1024, L=L, dev_rows=dev_rows, host_rows=host_rows)
+    pool, bufs, devs = _small_pool(R=4, S=1024, L=L, dev_rows=dev_rows, host_rows=host_rows, rb=rb)
     try:
         rng = np.random.default_rng(count)
         d = rng.integers(0, dev_rows, size=count).astype(np.int32)
@@ -40,10 +42,10 @@ def test_mirror_rows_vs_oracle(count):
             d[1] = -1                      # padding
             d[2] = dev_rows + 3            # past the device pool: tripwire
             h[3] = host_rows               # past the host pool: tripwire
-        ost = OracleState(R=4, S=1024, L=L, row_bytes=RB, dev_pool_rows=dev_rows)
+        ost = OracleState(R=4, S=1024, L=L, row_bytes=rb, dev_pool_rows=dev_rows)
         for l in range(L):
             ost.dev_pools[l][:] = devs[l].cpu().numpy()
-        ohost = [b.numpy((host_rows, RB)).copy() for b in bufs]
+        ohost = [b.numpy((host_rows, rb)).copy() for b in bufs]
         oracle_mirror_rows(ost, dev_rows=d, host_rows=h, host_pools=ohost,
                            host_pool_rows=[host_rows] * L, validate=True)
         stats = torch.zeros(5, dtype=torch.int64, device="cuda")
@@ -51,15 +53,15 @@ def test_mirror_rows_vs_oracle(count):
                                 stats=stats)
         torch.cuda.synchronize()
         for l in range(L):
-            assert np.array_equal(bufs[l].numpy((host_rows, RB)), ohost[l]), "layer %d" % l
+            assert np.array_equal(bufs[l].numpy((host_rows, rb)), ohost[l]), "layer %d" % l
         assert np.array_equal(stats.cpu().numpy().astype(np.uint64), ost.stats)
         # a layer range touches only its layers
         hs.hisparse_mirror_rows(pool, None, torch.from_numpy(d[:1].copy()).cuda(),
                                 torch.from_numpy(np.array([0], np.int64)).cuda(), 1, 2)
         torch.cuda.synchronize()
-        assert np.array_equal(bufs[0].numpy((host_rows, RB))[0], ohost[0][0])
+        assert np.array_equal(bufs[0].numpy((host_rows, rb))[0], ohost[0][0])
         if d[0] >= 0:
-            assert np.array_equal(bufs[1].numpy((host_rows, RB))[0], ost.dev_pools[1][d[0]])
+            assert np.array_equal(bufs[1].numpy((host_rows, rb))[0], ost.dev_pools[1][d[0]])
     finally:
         hs.hisparse_destroy_pool(pool)
         for b in bufs:
