@@ -110,9 +110,10 @@ def test_resolve_steps_bounds():
 @pytest.mark.parametrize("seed", range(16))
 def test_resolve_steps_random_vs_oracle(seed):
     """Seeded random verification-step calls: 1-4 steps per call, random k,
-    batch and layers, hot slots between steps * k and (steps + 2) * k; every
-    position's row IDs, and the state after each call, bit-exact against the
-    same positions as consecutive oracle calls."""
+    batch and layers, hot slots between steps * k and (steps + 2) * k, with or
+    without a resident tail (pages of 16 or 24 tokens) and a padding row;
+    every position's row IDs, and the state after each call, bit-exact
+    against the same positions as consecutive oracle calls."""
     rng = np.random.default_rng(800 + seed)
     Q = int(rng.integers(1, 5))
     D = int(rng.integers(2, 4))
@@ -122,9 +123,13 @@ def test_resolve_steps_random_vs_oracle(seed):
     S = Q * k + int(rng.integers(0, 2 * k + 1))
     n0 = [int(v) for v in rng.integers(1, 8 * S, size=B)]
     keep = int(rng.integers(0, k + 1))
-    print("[steps random %d] Q=%d D=%d k=%d S=%d B=%d L=%d" % (seed, Q, D, k, S, B, L), flush=True)
+    P = int(rng.choice([0, 0, 16, 24]))
+    tail = int(rng.choice([0, 2, 4])) * P
+    pad = int(rng.integers(0, 2))
+    print("[steps random %d] Q=%d D=%d k=%d S=%d B=%d L=%d P=%d tail=%d pad=%d"
+          % (seed, Q, D, k, S, B, L, P, tail, pad), flush=True)
     w = synth("mtprand%d" % seed, 900 + seed, R=B + 1, S=S, k=k, steps=Q * D, n0=n0, L=L, grow=1,
-              keep=keep)
+              keep=keep, P=P, resident_tail=tail, padding_rows=pad)
     pair = Pair(w, make_host_pools(w), max_steps=Q)
     try:
         out = torch.empty((Q, w.B, w.k), dtype=torch.int32, device="cuda")
