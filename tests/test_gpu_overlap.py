@@ -20,18 +20,21 @@ SCALE = 1.0 / math.sqrt(192.0)
 # split partials alternate between two workspace halves, so odd and even
 # counts end on different halves); 260 batch rows of one key split each make
 # the decode alone fill the CUs, so the copy and combine workgroups of each
-# launch run after it.
-@pytest.mark.parametrize("B,L,corrupt", [(4, 3, False), (9, 3, False), (9, 3, True), (5, 1, False),
-                                         (6, 2, True), (7, 5, False), (260, 2, False)])
-def test_overlapped_layers_match_sequential(B, L, corrupt):
+# launch run after it.  The last two: padding batch rows among the requests,
+# and 144 heads (a full and a partial head group of 128).
+@pytest.mark.parametrize("B,L,corrupt,pad,H", [(4, 3, False, 0, 32), (9, 3, False, 0, 32),
+                                               (9, 3, True, 0, 32), (5, 1, False, 0, 32),
+                                               (6, 2, True, 0, 32), (7, 5, False, 0, 32),
+                                               (260, 2, False, 0, 32), (8, 3, False, 3, 144),
+                                               (3, 2, True, 2, 144)])
+def test_overlapped_layers_match_sequential(B, L, corrupt, pad, H):
     """With `corrupt`, some host rows are out of range (negative or past the
     pool), so the layer copy's zero fill and tripwire count are compared
     too."""
-    print("[overlap] B=%d L=%d corrupt=%s" % (B, L, corrupt), flush=True)
-    H = 32
+    print("[overlap] B=%d L=%d corrupt=%s pad=%d H=%d" % (B, L, corrupt, pad, H), flush=True)
     n0 = [3000 + 700 * b for b in range(B)] if B <= 64 else [600 + 7 * b for b in range(B)]
     w = synth("ovl", 70 + B, R=B, S=256, k=128, steps=3, n0=n0, L=L, grow=1, keep=80, recent=16,
-              recent_window=64)
+              recent_window=64, padding_rows=pad)
     if corrupt:   # every request is past S, so admission copies no host rows
         rng = np.random.default_rng(12)
         locs = w.host_cache_locs
