@@ -255,6 +255,108 @@ def mixed_residency_legs(hs, torch, stream, reuses=(0.5, 0.9, 0.99, 1.0)):
     return res
 
 
+def long_context_leg(hs, torch, stream):
+    """1M-token context with index-shared layers: 16 requests of 1,048,576
+    tokens, 6144 hot slots (8 per thread in the plan kernel), top-2048,
+    4 layers that share one plan, each layer with its own 11.0 GB host pool
+    (44 GB pinned), 32 steps.  Per step: the last 512 positions and 48
+    Zipf(1.1)-drawn 32-token blocks.  Step 0 (every slot empty) timed alone;
+    steps 1..31 through hisparse_resolve (one launch per step: plan and the
+    4 layers' copies); then the same steps replayed from the state after
+    step 0 through the plan-only entry point, for the hit path against HBM."""
+    from workloads import config4_indexshare_1m, admission, fill_host_rows_uniform
+    dev = torch.device("cuda")
+    w = config4_indexshare_1m()
+    log("long context: %d host pools of %.1f GB pinned" % (w.L, w.host_pool_rows * ROW_BYTES / 1e9))
+    hosts = [hs.HostBuffer(w.host_pool_rows * ROW_BYTES) for _ in range(w.L)]
+    for l, h in enumerate(hosts):
+        fill_host_rows_uniform(h.torch((w.host_pool_rows, ROW_BYTES)), seed=40 + l, gen_device="cuda")
+    pools = [torch.zeros((w.dev_pool_rows, w.row_bytes), dtype=torch.uint8, device=dev)
+             for _ in range(w.L)]
+    cfg = hs.PoolConfig(max_requests=w.R, slots=w.S, max_top_k=w.k, max_batch=w.B,
+                        row_bytes=w.row_bytes, num_layers=w.L, max_seq_len=w.max_seq_len)
+    pool = hs.hisparse_init_pool(cfg, hosts, [w.host_pool_rows] * w.L, pools, w.dev_pool_rows)
+    st0, lru0, clk0, dst, src = admission(w)
+    assert len(dst) == 0  # every request starts longer than its hot buffer
+    locs = torch.from_numpy(w.host_cache_locs).to(dev)
+    req = torch.from_numpy(w.req_idx).to(dev)
+    topk = torch.from_numpy(w.top_k).to(dev)
+    seq = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    st, lru, clk = (torch.from_numpy(x).to(dev) for x in (st0, lru0, clk0))
+    stats = torch.zeros(5, dtype=torch.int64, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+
+    def resolve(i, plan_only=False, with_stats=True):
+        fn = hs.hisparse_resolve_plan if plan_only else hs.hisparse_resolve
+        fn(pool, stream, w.B, w.k, req, topk[i], seq[i], locs, None, st, lru, clk, out,
+           stats if with_stats else None)
+
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    resolve(0)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    s0 = stats.cpu().numpy().astype(np.int64)
+    snap = (st.clone(), lru.clone(), clk.clone())
+    ev[2].record(stream)
+    for i in range(1, w.steps):
+        resolve(i)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    s1 = stats.cpu().numpy().astype(np.int64)
+    st.copy_(snap[0]); lru.copy_(snap[1]); clk.copy_(snap[2])
+    torch.cuda.synchronize()
+    ev[4].record(stream)
+    for i in range(1, w.steps):
+        resolve(i, plan_only=True, with_stats=False)
+    ev[5].record(stream)
+    torch.cuda.synchronize()
+    # the same steps through the split entry points (plan, then the copy
+    # kernel over all layers), for comparison with the single launch
+    st.copy_(snap[0]); lru.copy_(snap[1]); clk.copy_(snap[2])
+    torch.cuda.synchronize()
+    ev[6].record(stream)
+    for i in range(1, w.steps):
+        resolve(i, plan_only=True, with_stats=False)
+        hs.hisparse_gather_copy(pool, stream, w.B)
+    ev[7].record(stream)
+    torch.cuda.synchronize()
+    n = w.steps - 1
+    cold_ms = ev[0].elapsed_time(ev[1])
+    step_ms = ev[2].elapsed_time(ev[3]) / n
+    plan_ms = ev[4].elapsed_time(ev[5]) / n
+    split_ms = ev[6].elapsed_time(ev[7]) / n
+    hits, misses, resident, fast, trips = [int(x) for x in (s1 - s0)]
+    valid = hits + misses + resident + fast
+    # per step: top-k read + row IDs written (8k) and slot map + stamps read
+    # (8S) per row, 16 B per row, a stamp per touched slot, host location +
+    # map write per miss
+    plan_bytes = w.B * (8 * w.k + 8 * w.S) + w.B * 16 + (4 * (hits + misses) + 12 * misses) / n
+    link_bytes = misses * ROW_BYTES * w.L / n
+    res = {
+        "cold_step0_ms": cold_ms, "cold_step0_misses": int(s0[1]),
+        "cold_step0_copy_gbs": int(s0[1]) * ROW_BYTES * w.L / (cold_ms * 1e-3) / 1e9,
+        "step_ms": step_ms, "rows_resolved_per_s": valid / n / (step_ms * 1e-3),
+        "hits_per_step": hits / n, "misses_per_step": misses / n, "tripwires": trips,
+        "miss_copy_gbs": link_bytes / (step_ms * 1e-3) / 1e9,
+        "plan_only_us": plan_ms * 1e3, "plan_algorithmic_bytes": plan_bytes,
+        "plan_hbm_gbs": plan_bytes / (plan_ms * 1e-3) / 1e9,
+        "plan_hbm_frac": plan_bytes / (plan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "split_step_ms": split_ms,
+        "workload": ("16 requests x 1,048,576 tokens, 6144 slots, top-2048 (last 512 positions + "
+                     "48 Zipf(1.1) blocks of 32), 4 layers of 11.0 GB host pools, 32 steps from "
+                     "cold; steps 1..31 timed"),
+    }
+    log("long context: step %.3f ms, plan %.1f us, misses/step %.0f"
+        % (step_ms, plan_ms * 1e3, misses / n))
+    hs.hisparse_destroy_pool(pool)
+    del pools
+    for h in hosts:
+        h.free()
+    return res
+
+
 def next_rows_legs(w, g, hs, torch, stream, host_buf, snap, restore, warmup, steps):
     """The rows after the resolver: row mirror, invalidation, the verification
     steps of speculative decoding and the copy/decode overlap over layers.
@@ -669,6 +771,9 @@ def main():
     ap.add_argument("--plan-phases", action="store_true",
                     help="only the plan kernel's phase trace (diagnostic library) over the "
                          "timed steps and the floor kernels of its launch shape")
+    ap.add_argument("--long-context", action="store_true",
+                    help="only the 1M-token, 4-layer workload (44 GB pinned): cold step, "
+                         "31 timed steps and the plan-only replays")
     args = ap.parse_args()
     if args.plan_phases:
         os.environ["HISPARSE_LIBRARY"] = "diag"   # read when the package is imported
@@ -695,6 +800,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.long_context:
+        res = long_context_leg(hs, torch, torch.cuda.current_stream())
+        res.update({"metric": "long-context resolve step", "n_gpus": 1,
+                    "config": {"workload": "indexshare_1m"}})
+        print(json.dumps(res), flush=True)
+        return
     total_steps = args.warmup + args.steps
     log("generating workload (%d steps)" % total_steps)
     w = config2_dsa_decode(steps=total_steps)
