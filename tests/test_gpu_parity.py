@@ -89,6 +89,19 @@ def test_resident_page_sizes(mode, P, tail):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("S", [1, 2])
+def test_smallest_hot_buffers(mode, S):
+    """One or two hot slots with top-k = S: rows of 1 token (fast path), rows
+    that leave it, long rows where every step's miss evicts the previous
+    token, a padding row; nine rows, so the single-call entry point fuses."""
+    print("[smallest %s] S=k=%d" % (mode, S), flush=True)
+    w = synth("tiny%d" % S, 61 + S, R=9, S=S, k=S, steps=6,
+              n0=[1, S, S + 1, 40, 900, 2, 7, 3000, 1], grow=1, keep=S // 2, padding_rows=1)
+    stats = run_parity(w, mode=mode)
+    assert stats[1] > 0 and stats[3] > 0  # misses, and fast-path entries
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_top_k_equals_slots(mode):
     print("[k=S %s] S=k=2048" % mode, flush=True)
     w = synth("kS", 24, R=8, S=2048, k=2048, steps=4,
