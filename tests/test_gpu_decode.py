@@ -222,6 +222,33 @@ def test_decode_all_invalid_gives_zero():
     assert np.all(got == 0)
 
 
+def test_decode_zero_keys_writes_zeros():
+    """top_k = 0: no entry to attend to, so every output is 0 (written over
+    a NaN-filled buffer), through the pool and the allocation-free entry
+    points."""
+    B, H = 3, 144
+    dev = torch.empty((64, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 5, gen_device="cuda")
+    q = make_queries(B, H, seed=2, device="cuda")
+    locs = torch.empty((B, 0), dtype=torch.int32, device="cuda")
+    hb = hs.HostBuffer(656 * 16)
+    cfg = hs.PoolConfig(max_requests=1, slots=16, max_top_k=16, max_batch=B, max_seq_len=16,
+                        max_heads=H)
+    pool = hs.hisparse_init_pool(cfg, [hb], [16], [dev], dev.shape[0])
+    try:
+        for noalloc in (False, True):
+            out = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            if noalloc:
+                hs.hisparse_sparse_mla_decode_noalloc(None, B, H, 0, dev, q, locs, SCALE, out)
+            else:
+                hs.hisparse_sparse_mla_decode(pool, None, B, H, 0, 0, q, locs, SCALE, out)
+            torch.cuda.synchronize()
+            assert torch.equal(out.float(), torch.zeros((B, H, 512), device="cuda")), noalloc
+    finally:
+        hs.hisparse_destroy_pool(pool)
+        hb.free()
+
+
 def test_decode_after_resolver():
     """Resolver output feeds the decode on the same pool (small DSA-like)."""
     print("[decode+resolve]", flush=True)
