@@ -250,3 +250,36 @@ def test_invalidate_then_resolve_refetches():
         assert pair.ost.stats[1] - before[1] >= 20
     finally:
         pair.close()
+
+
+def test_empty_calls_change_nothing():
+    """Zero entries: the mirror, both invalidations and an empty layer range
+    return without touching host pools, device pools or state."""
+    R, S, n, L = 4, 256, 600, 2
+    pool, bufs, devs = _small_pool(R=R, S=S, L=L, dev_rows=R * S, host_rows=700, max_seq_len=n)
+    try:
+        rng = np.random.default_rng(3)
+        st, lru = _random_state(rng, R, S, n)
+        gst, glru = torch.from_numpy(st).cuda(), torch.from_numpy(lru).cuda()
+        locs = torch.from_numpy(rng.integers(0, 700, size=(R, n)).astype(np.int64)).cuda()
+        host0 = [b.numpy((700, RB)).copy() for b in bufs]
+        dev0 = [d.clone() for d in devs]
+        stats = torch.zeros(5, dtype=torch.int64, device="cuda")
+        e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+        e64 = torch.empty(0, dtype=torch.int64, device="cuda")
+        hs.hisparse_mirror_rows(pool, None, e32, e64, stats=stats)
+        one = torch.zeros(1, dtype=torch.int32, device="cuda")
+        hs.hisparse_mirror_rows(pool, None, one, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                                1, 1, stats=stats)  # an empty layer range
+        hs.hisparse_invalidate_tokens(pool, None, e32, e32, e32, gst, glru, stats)
+        hs.hisparse_invalidate_host_rows(pool, None, e64, locs, gst, glru)
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert np.array_equal(bufs[l].numpy((700, RB)), host0[l])
+            assert torch.equal(devs[l], dev0[l])
+        assert np.array_equal(gst.cpu().numpy(), st) and np.array_equal(glru.cpu().numpy(), lru)
+        assert int(stats.sum().item()) == 0
+    finally:
+        hs.hisparse_destroy_pool(pool)
+        for b in bufs:
+            b.free()
