@@ -114,6 +114,47 @@ def test_decode_replayed_from_a_graph():
         hb.free()
 
 
+def test_noalloc_decode_replayed_from_a_graph():
+    """The allocation-free decode captured in a graph (after one eager call,
+    which looks up its static workspace on this device) and replayed over
+    three query sets, twice: every replay equals the eager call."""
+    print("[graph] allocation-free decode", flush=True)
+    B, H, k, rows = 5, 144, 600, 1500
+    dev = torch.empty((rows, 656), dtype=torch.uint8, device="cuda")
+    fill_host_rows_mla(dev, 9, gen_device="cuda")
+    rng = np.random.default_rng(9)
+    locs = torch.from_numpy(rng.integers(-1, rows, size=(B, k)).astype(np.int32)).cuda()
+    scale = 1.0 / math.sqrt(192.0)
+    qs = [make_queries(B, H, seed=40 + t, device="cuda") for t in range(3)]
+    want = []
+    for q in qs:
+        o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+        hs.hisparse_sparse_mla_decode_noalloc(None, B, H, k, dev, q, locs, scale, o)
+        want.append(o)
+    torch.cuda.synchronize()
+    q_s = qs[0].clone()
+    out_s = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        hs.hisparse_sparse_mla_decode_noalloc(None, B, H, k, dev, q_s, locs, scale, out_s)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for t, q in enumerate(qs):
+            q_s.copy_(q)
+            out_s.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_s, want[t]), "replay %d of query set %d differs" % (rep, t)
+            # an eager call between replays, on the same static workspace
+            o = torch.empty_like(out_s)
+            hs.hisparse_sparse_mla_decode_noalloc(None, B, H, k, dev, qs[(t + 1) % 3], locs, scale, o)
+            torch.cuda.synchronize()
+            assert torch.equal(o, want[(t + 1) % 3])
+    print("[graph] 6 allocation-free decode replays equal the eager calls", flush=True)
+
+
 def test_overlapped_layers_replayed_from_a_graph():
     """Plan plus the overlapped per-layer copy and decode (every launch on
     the caller's stream) captured once, before the pool has run anything,
