@@ -360,15 +360,20 @@ def check_step_invariants(w, step, before, after, out, host_pools, dev_pools, c_
                     assert np.array_equal(dev_pools[l][r * S + s], host_pools[l][h])
 
 
-def test_step_invariants_on_small_workload():
+@pytest.mark.parametrize("row_bytes,L", [(656, 1), (16, 2), (2064, 2)])
+def test_step_invariants_on_small_workload(row_bytes, L):
+    """Every step's invariants, including every hot row's bytes against its
+    token's host row in every layer, at row widths of one 16-byte unit up to
+    129 units."""
     from workloads import synth, admission, decode_writes, fill_host_rows_uniform
     w = synth("small", 11, R=6, S=64, k=24, steps=12, n0=[300, 500, 40, 64, 1000, 62],
-              grow=1, keep=20, recent=2, recent_window=30, padding_rows=1)
-    hostt = [torch.empty((w.host_pool_rows, 656), dtype=torch.uint8) for _ in range(w.L)]
+              grow=1, keep=20, recent=2, recent_window=30, padding_rows=1, L=L)
+    w.row_bytes = row_bytes
+    hostt = [torch.empty((w.host_pool_rows, row_bytes), dtype=torch.uint8) for _ in range(w.L)]
     for l, h in enumerate(hostt):
         fill_host_rows_uniform(h, seed=50 + l)
     host = [h.numpy() for h in hostt]
-    st = OracleState(R=w.R, S=w.S, L=w.L, row_bytes=656, dev_pool_rows=w.dev_pool_rows)
+    st = OracleState(R=w.R, S=w.S, L=w.L, row_bytes=row_bytes, dev_pool_rows=w.dev_pool_rows)
     s0, l0, c0, dst, src = admission(w)
     st.slot_tokens[:], st.lru_slots[:], st.lru_clock[:] = s0, l0, c0
     for l in range(w.L):
@@ -383,7 +388,7 @@ def test_step_invariants_on_small_workload():
                              req_idx=w.req_idx, top_k_tokens=w.top_k[step],
                              seq_lens=w.seq_lens[step], host_cache_locs=w.host_cache_locs,
                              block_table=None, host_pools=host,
-                             host_pool_rows=[w.host_pool_rows], validate=True)
+                             host_pool_rows=[w.host_pool_rows] * w.L, validate=True)
         check_step_invariants(w, step, before, (st.slot_tokens, st.lru_slots), out, host,
                               st.dev_pools, c_exp)
     assert st.stats[4] == 0
@@ -431,6 +436,27 @@ def test_attention_vs_torch_float64():
     scale = float(np.float32(1.0 / math.sqrt(192.0)))
     got = oracle_sparse_mla_decode(q_bits, locs, pool.numpy(), scale)
     ref = _torch_reference(q_bits, locs, pool, scale)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("row_bytes", [672, 1024])
+def test_attention_padded_rows_vs_torch_float64(row_bytes):
+    """Rows stored at a larger stride: the oracle reads each row's 656-byte
+    record at that stride and never the padding (all 0xFF, NaN codes), so it
+    equals torch's float64 attention over the unpadded rows."""
+    pool = _mla_rows(200, seed=8)
+    padded = torch.full((200, row_bytes), 0xFF, dtype=torch.uint8)
+    padded[:, :656] = pool
+    rng = np.random.default_rng(row_bytes)
+    B, H, k = 2, 8, 29
+    locs = np.stack([rng.choice(200, size=k, replace=False) for _ in range(B)]).astype(np.int32)
+    locs[0, ::4] = -1
+    q = torch.randn((B, H, 576), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().astype(np.uint16)
+    scale = float(np.float32(1.0 / math.sqrt(192.0)))
+    got = oracle_sparse_mla_decode(q_bits, locs, padded.numpy(), scale, row_bytes=row_bytes)
+    ref = _torch_reference(q_bits, locs, pool, scale)
+    assert np.isfinite(got).all()
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
