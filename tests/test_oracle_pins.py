@@ -266,20 +266,22 @@ def test_exhaustive_three_steps_vs_naive(S, k, n):
     _run_both(B, S, 0, n, steps)
 
 
+@pytest.mark.parametrize("P", [4, 3, 5])
 @pytest.mark.parametrize("seed", range(6))
-def test_random_corrupt_state_vs_naive(seed):
+def test_random_corrupt_state_vs_naive(seed, P):
     """Random initial state including empty markers below -1, one position in
     two slots, stamps above the clock and negative stamps, with a resident
-    block table (some entries out of range), padding rows, request indices
-    past R, out-of-range host rows and invalid top-k entries."""
-    rng = np.random.default_rng(100 + seed)
-    R, S, P, n, k, L = 6, 8, 4, 40, 6, 2
+    block table (some entries out of range; pages of 3, 4 or 5 tokens, the
+    last page partial for 3), padding rows, request indices past R,
+    out-of-range host rows and invalid top-k entries."""
+    rng = np.random.default_rng(100 + seed + 1000 * (P != 4) * P)
+    R, S, n, k, L = 6, 8, 40, 6, 2
     st0 = rng.integers(-3, n + 3, size=(R, S)).astype(np.int32)
     st0[0, 1] = st0[0, 5] = 11          # one position held twice
     lru0 = rng.integers(-2, 6, size=(R, S)).astype(np.int32)
     clk0 = rng.integers(0, 4, size=R).astype(np.int32)
     resident_pages = 3
-    bt = rng.integers(-1, resident_pages + 2, size=(R, n // P)).astype(np.int32)
+    bt = rng.integers(-1, resident_pages + 2, size=(R, -(-n // P))).astype(np.int32)
     bt[bt < 1] = -1
     bt[bt >= 1] -= 1                    # some >= resident_pages (corrupt)
     locs = rng.integers(-2, R * n + 5, size=(R, n)).astype(np.int64)
