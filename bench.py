@@ -255,6 +255,65 @@ def mixed_residency_legs(hs, torch, stream, reuses=(0.5, 0.9, 0.99, 1.0)):
     return res
 
 
+def plan_batch_sweep(hs, torch, stream, batches=(64, 128, 256), steps=24, warm=4):
+    """The plan kernel (one workgroup of 1024 threads per request) as the
+    batch grows: the DSA-decode workload with 64, 128 and 256 long rows
+    (seq_len 32768-131072, top-2048, 4096 slots, no fast-path rows).  Per
+    batch: `warm` steps through hisparse_resolve to leave the cold start, the
+    rest through it with stats (hits and misses for the algorithmic bytes),
+    then the same steps replayed plan-only from the state before them."""
+    from workloads import config2_dsa_decode, fill_host_rows_uniform
+    res = {}
+    for nb in batches:
+        w = config2_dsa_decode(steps=steps, long_rows=nb, short_rows=0)
+        host = hs.HostBuffer(w.host_pool_rows * ROW_BYTES)
+        fill_host_rows_uniform(host.torch((w.host_pool_rows, ROW_BYTES)), seed=7, gen_device="cuda")
+        g = setup_gpu(w, torch, hs, host)
+
+        def resolve(i, plan_only=False, with_stats=True):
+            fn = hs.hisparse_resolve_plan if plan_only else hs.hisparse_resolve
+            fn(g["pool"], stream, w.B, w.k, g["req"], g["topk"][i], g["seq"][i], g["locs"], None,
+               g["st"], g["lru"], g["clk"], g["out"], g["stats"] if with_stats else None)
+
+        for i in range(warm):
+            resolve(i, with_stats=False)
+        torch.cuda.synchronize()
+        snap = (g["st"].clone(), g["lru"].clone(), g["clk"].clone())
+        g["stats"].zero_()
+        for i in range(warm, w.steps):
+            resolve(i)
+        torch.cuda.synchronize()
+        hits, misses, resident, fast, trips = [int(x) for x in g["stats"].cpu().numpy()]
+        g["st"].copy_(snap[0]); g["lru"].copy_(snap[1]); g["clk"].copy_(snap[2])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(warm, w.steps):
+            resolve(i, plan_only=True, with_stats=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = w.steps - warm
+        plan_ms = e0.elapsed_time(e1) / n
+        # as for the DSA-decode plan: top-k read + row IDs written (8k) and
+        # slot map + stamps read (8S) per row, 16 B per row, a stamp per
+        # touched slot, host location + map write per miss
+        plan_bytes = w.B * (8 * w.k + 8 * w.S) + w.B * 16 + (4 * (hits + misses) + 12 * misses) / n
+        res["rows_%d" % nb] = {
+            "plan_only_us": plan_ms * 1e3, "plan_algorithmic_bytes": plan_bytes,
+            "plan_hbm_gbs": plan_bytes / (plan_ms * 1e-3) / 1e9,
+            "plan_hbm_frac": plan_bytes / (plan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "misses_per_step": misses / n, "tripwires": trips,
+        }
+        log("plan batch sweep: %d rows, plan %.1f us, %.2f MB" % (nb, plan_ms * 1e3, plan_bytes / 1e6))
+        hs.hisparse_destroy_pool(g["pool"])
+        del g
+        torch.cuda.empty_cache()
+        host.free()
+    res["workload"] = ("dsa_decode long rows only (seq_len 32768-131072, top-2048, 4096 slots), "
+                       "%d steps, steps %d..%d timed plan-only" % (steps, warm, steps - 1))
+    return res
+
+
 def long_context_leg(hs, torch, stream):
     """1M-token context with index-shared layers: 16 requests of 1,048,576
     tokens, 6144 hot slots (8 per thread in the plan kernel), top-2048,
@@ -777,6 +836,8 @@ def main():
     ap.add_argument("--plan-phases", action="store_true",
                     help="only the plan kernel's phase trace (diagnostic library) over the "
                          "timed steps and the floor kernels of its launch shape")
+    ap.add_argument("--plan-batch-sweep", action="store_true",
+                    help="only the plan kernel at 64, 128 and 256 long rows (plan-only replays)")
     ap.add_argument("--long-context", action="store_true",
                     help="only the 1M-token, 4-layer workload (44 GB pinned): cold step, "
                          "31 timed steps and the plan-only replays")
@@ -806,6 +867,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.plan_batch_sweep:
+        res = plan_batch_sweep(hs, torch, torch.cuda.current_stream())
+        res.update({"metric": "plan kernel time against batch", "n_gpus": 1,
+                    "config": {"workload": "dsa_decode_long_rows"}})
+        print(json.dumps(res), flush=True)
+        return
     if args.long_context:
         res = long_context_leg(hs, torch, torch.cuda.current_stream())
         res.update({"metric": "long-context resolve step", "n_gpus": 1,
